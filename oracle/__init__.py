@@ -1,0 +1,15 @@
+"""CPU float64 oracle for exact attention: test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. The product (the HIP library and its binding) never does.
+"""
+from .attention import (  # noqa: F401
+    attention_backward,
+    attention_forward,
+    attention_forward_online,
+    attention_rows,
+    backward_delta,
+    online_softmax_stats,
+    scores,
+    softmax_stats,
+)

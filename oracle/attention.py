@@ -1,0 +1,207 @@
+"""CPU float64 oracle for exact attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+link this module: only the tests, the smoke check and the CPU-baseline leg of
+the benchmark use it. It shares no code with the HIP path; its inputs are
+plain numpy arrays (callers upcast bf16/fp32 storage to float64 exactly).
+
+Sources (page titles; sections named after each function):
+  [Lab06]  "Lab 06 - Attention kernels: online softmax -> FlashAttention -> Triton"
+  [FA2nb]  "Triton FlashAttention-2 forward" (notebook)
+  [FAopt]  "Flash Attention and Kernel Optimization" (llm-from-scratch docs)
+
+Conventions (the plainest reading the pages support):
+  * Layout (B, H, T, D); one sequence length T shared by queries and keys.
+  * S = scale * Q K^T; the scale is inside the softmax, hence inside LSE.
+  * causal: key j is visible to query i iff j <= i (top-left aligned).
+  * LSE is the natural-log log-sum-exp of each row of S, with no epsilon.
+  * Output dtype handling is the caller's business: this module returns
+    float64 everywhere.
+
+Every function here is pinned by the not-gpu tests against something other
+than itself (closed forms, brute force, torch float64 CPU routines, finite
+differences); see tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_ROW_CHUNK = 2048  # rows of S materialised at once (bounds memory at long T)
+
+
+def _check_qkv(q, k, v):
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype != np.float64:
+            raise TypeError(f"oracle expects float64 arrays, {name} is {x.dtype}")
+        if x.ndim != 4:
+            raise ValueError(f"{name} must be (B, H, T, D), got shape {x.shape}")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q/k/v shapes differ: {q.shape} {k.shape} {v.shape}")
+
+
+def scores(q_bh: np.ndarray, k_bh: np.ndarray, scale: float, causal: bool,
+           rows: np.ndarray | None = None) -> np.ndarray:
+    """Scaled, masked score rows S[i, :] = scale * q_i . k_j for one (b, h).
+
+    [Lab06] section 3 (S = Q K^T * scale per tile); [FA2nb] "The kernel" (the
+    causal rule keeps key n for query m when m >= n). Masked entries are -inf.
+    `rows` selects query indices (default: all).
+    """
+    T = k_bh.shape[0]
+    if rows is None:
+        rows = np.arange(q_bh.shape[0])
+    s = (q_bh[rows] @ k_bh.T) * scale
+    if causal:
+        keys = np.arange(T)
+        s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+    return s
+
+
+def softmax_stats(s: np.ndarray):
+    """Row max m, row sum l = sum_j exp(S_ij - m_i) and LSE = m + ln l.
+
+    [Lab06] section 2: logsumexp equals m + log l. Two-pass definition (max
+    first, then the shifted sum), not the online recurrence.
+    """
+    m = np.max(s, axis=-1)
+    l = np.sum(np.exp(s - m[..., None]), axis=-1)
+    return m, l, m + np.log(l)
+
+
+def attention_rows(q_bh, k_bh, v_bh, scale: float, causal: bool, rows: np.ndarray):
+    """O and LSE for selected query rows of one (b, h), by the definition.
+
+    O_i = sum_j softmax(S_i)_j V_j with S materialised for those rows only.
+    [Lab06] section 1 (the dense computation the method reproduces exactly)
+    and section 3 (O and LSE are what the tiled method returns).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scores(q_bh, k_bh, scale, causal, rows)
+    _, _, lse = softmax_stats(s)
+    p = np.exp(s - lse[:, None])
+    return p @ v_bh, lse
+
+
+def attention_forward(q, k, v, scale: float, causal: bool):
+    """Exact attention forward for every (b, h): returns (O, LSE) in float64.
+
+    O has shape (B, H, T, D), LSE has shape (B, H, T). S is materialised one
+    (b, h) at a time in chunks of query rows, with a two-pass softmax.
+    """
+    _check_qkv(q, k, v)
+    B, H, T, D = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, T, _ROW_CHUNK):
+                rows = np.arange(r0, min(T, r0 + _ROW_CHUNK))
+                o[b, h, rows], lse[b, h, rows] = attention_rows(
+                    q[b, h], k[b, h], v[b, h], scale, causal, rows)
+    return o, lse
+
+
+def online_softmax_stats(x: np.ndarray, block: int):
+    """Online (streaming) max and shifted sum over the last axis.
+
+    [Lab06] section 2 (Milakov & Gimelshein): visit the values block by block,
+    keep the running max m and l = sum exp(x - m); when a block raises the max
+    to m', multiply l by exp(m - m') before adding the block's own terms.
+    Returns (m, l, m + ln l). The first block starts from m = -inf, l = 0, and
+    the exp(m - m') factor is taken as 0 while m is still -inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = np.full(x.shape[:-1], -np.inf)
+    l = np.zeros(x.shape[:-1])
+    n = x.shape[-1]
+    for j0 in range(0, n, block):
+        blk = x[..., j0:j0 + block]
+        m_new = np.maximum(m, np.max(blk, axis=-1))
+        safe = np.where(np.isneginf(m_new), 0.0, m_new)
+        alpha = np.where(np.isneginf(m), 0.0, np.exp(m - safe))
+        l = l * alpha + np.sum(np.exp(blk - safe[..., None]), axis=-1)
+        m = m_new
+    return m, l, m + np.log(l)
+
+
+def attention_forward_online(q, k, v, scale: float, causal: bool,
+                             block_m: int, block_n: int):
+    """The tiled FlashAttention forward recurrence, in float64.
+
+    [Lab06] section 3; [FA2nb] "The kernel"; [FAopt] "Running softmax state".
+    For each query tile keep (m, l, acc) per row; for each key tile: S tile,
+    m' = max(m, rowmax S), P~ = exp(S - m'), acc <- acc*exp(m - m') + P~ V,
+    l <- l*exp(m - m') + rowsum P~. Finish with O = acc / l and
+    LSE = m + ln l. Causal: key tiles that lie wholly after the tile's last
+    query are not visited ([Lab06] section 3 figure and "Common bugs": the
+    last needed key tile is the one holding query i1 - 1); the diagonal tile
+    is masked element-wise. Block sizes need not divide T.
+
+    Exists to show that the recurrence reaches the two-pass result; the GPU
+    parity tests compare against attention_forward / attention_rows.
+    """
+    _check_qkv(q, k, v)
+    B, H, T, D = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            for i0 in range(0, T, block_m):
+                i1 = min(T, i0 + block_m)
+                qi = q[b, h, i0:i1]
+                m = np.full(i1 - i0, -np.inf)
+                l = np.zeros(i1 - i0)
+                acc = np.zeros((i1 - i0, D))
+                j_end = i1 if causal else T          # keys [0, j_end) can be visible
+                for j0 in range(0, j_end, block_n):
+                    j1 = min(T, j0 + block_n)
+                    s = (qi @ k[b, h, j0:j1].T) * scale
+                    if causal:
+                        qi_idx = np.arange(i0, i1)[:, None]
+                        kj_idx = np.arange(j0, j1)[None, :]
+                        s = np.where(kj_idx <= qi_idx, s, -np.inf)
+                    m_new = np.maximum(m, np.max(s, axis=1))
+                    safe = np.where(np.isneginf(m_new), 0.0, m_new)
+                    alpha = np.where(np.isneginf(m), 0.0, np.exp(m - safe))
+                    p = np.exp(s - safe[:, None])
+                    acc = acc * alpha[:, None] + p @ v[b, h, j0:j1]
+                    l = l * alpha + np.sum(p, axis=1)
+                    m = m_new
+                o[b, h, i0:i1] = acc / l[:, None]
+                lse[b, h, i0:i1] = m + np.log(l)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool):
+    """Exact attention backward, dense, for every (b, h).
+
+    [Lab06] section 4: P = exp(S - LSE) recomputed from the saved LSE;
+    dV = P^T dO; dP = dO V^T; D_i = rowsum(dO * O)_i; dS = P * (dP - D);
+    dQ = scale * dS K; dK = scale * dS^T Q. [FAopt] "Autograd Wrapper and
+    Backward Path" lists the same dense steps (rebuild S, mask, softmax, then
+    the five gradients). The mask is applied before the exponential, as in
+    the forward ([Lab06] "Common bugs"). o and lse must be the oracle's own
+    forward outputs (or exact equivalents).
+    Returns (dQ, dK, dV) in float64.
+    """
+    _check_qkv(q, k, v)
+    B, H, T, D = q.shape
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], scale, causal)
+            p = np.exp(s - lse[b, h][:, None])
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            dvec = np.sum(do[b, h] * o[b, h], axis=1)
+            ds = p * (dp - dvec[:, None])
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def backward_delta(o, do):
+    """D_i = sum_d dO_id * O_id ([Lab06] section 4 and "Check yourself" answer 6)."""
+    return np.sum(o * do, axis=-1)

@@ -1,0 +1,374 @@
+"""Pins for the CPU float64 oracle (runs without a GPU).
+
+Each check ties the oracle to something other than its own code: textbook or
+library routines (scipy's logsumexp, torch's float64 CPU attention and
+autograd), closed forms that follow from the definition, brute-force finite
+differences, and the identities the pages state. The mutation tests at the
+end plant plausible mistakes into the oracle (on the CPU) and confirm that at
+least one pin catches each.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import attention as oattn
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- online softmax
+@pytest.mark.parametrize("n", [1, 37, 128, 1000])
+@pytest.mark.parametrize("block", [7, 11, 16, 32])
+def test_online_softmax_matches_logsumexp(n, block):
+    x = _rand((5, n), seed=n * 31 + block) * 4.0
+    m, l, lse = oracle.online_softmax_stats(x, block)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(x, axis=-1), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(m, x.max(axis=-1))
+    # l is the shifted sum at the final max: it lies in [1, n]
+    assert np.all(l >= 1.0) and np.all(l <= n)
+
+
+def test_online_softmax_handles_growing_max():
+    # The maximum jumps from -40 to 1000 between blocks (Lab 06, "What to implement" item 1).
+    x = np.full((1, 64), -40.0)
+    x[0, 50] = 1000.0
+    for block in (7, 11, 16, 32):
+        m, l, lse = oracle.online_softmax_stats(x, block)
+        # closed form: 1000 + ln(1 + 63 e^{-1040}) == 1000 in float64
+        assert m[0] == 1000.0
+        assert l[0] == 1.0
+        assert lse[0] == 1000.0
+    # a gentler jump where every term still matters
+    y = np.concatenate([np.full(10, -40.0), np.full(10, 2.0)])[None]
+    expect = 2.0 + math.log(10.0 + 10.0 * math.exp(-42.0))
+    for block in (3, 7, 10, 11):
+        assert abs(oracle.online_softmax_stats(y, block)[2][0] - expect) < 1e-13
+
+
+def test_softmax_stats_two_pass_matches_scipy():
+    x = _rand((7, 333), seed=3) * 10
+    m, l, lse = oracle.softmax_stats(x)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(x, axis=-1), atol=1e-12, rtol=0)
+    # masked entries (-inf) contribute nothing
+    x[:, 100:] = -np.inf
+    np.testing.assert_allclose(oracle.softmax_stats(x)[2],
+                               scipy.special.logsumexp(x[:, :100], axis=-1), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- forward vs torch
+def _torch_attention(q, k, v, scale, causal):
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    s = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        T = q.shape[2]
+        mask = torch.ones(T, T, dtype=torch.bool).tril()
+        s = s.masked_fill(~mask, float("-inf"))
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 33, 8), (2, 3, 37, 16), (1, 1, 130, 64), (1, 1, 1, 4)])
+def test_forward_matches_torch_float64(shape, causal):
+    q, k, v = (_rand(shape, seed=i + 10 * shape[2]) for i in range(3))
+    scale = 1.0 / math.sqrt(shape[3])
+    o, lse = oracle.attention_forward(q, k, v, scale, causal)
+    o_t, lse_t = _torch_attention(q, k, v, scale, causal)
+    np.testing.assert_allclose(o, o_t, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_t, atol=1e-12, rtol=0)
+
+
+def test_forward_row_chunking_at_long_t(monkeypatch):
+    # row chunks must not change the result (a chunk boundary inside T)
+    monkeypatch.setattr(oattn, "_ROW_CHUNK", 13)
+    shape = (1, 1, 50, 8)
+    q, k, v = (_rand(shape, seed=70 + i) for i in range(3))
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, 0.3, causal)
+        o_t, lse_t = _torch_attention(q, k, v, 0.3, causal)
+        np.testing.assert_allclose(o, o_t, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(lse, lse_t, atol=1e-12, rtol=0)
+
+
+def test_rows_match_full_forward():
+    shape = (1, 1, 200, 32)
+    q, k, v = (_rand(shape, seed=90 + i) for i in range(3))
+    rows = np.array([0, 1, 63, 64, 127, 199])
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, 0.2, causal)
+        o_r, lse_r = oracle.attention_rows(q[0, 0], k[0, 0], v[0, 0], 0.2, causal, rows)
+        # BLAS may block a subset of rows differently: agree to rounding
+        np.testing.assert_allclose(o_r, o[0, 0, rows], atol=1e-14, rtol=0)
+        np.testing.assert_allclose(lse_r, lse[0, 0, rows], atol=1e-14, rtol=0)
+
+
+# ---------------------------------------------------------------- online tiled = two-pass
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1, 16, 33, 37, 64])
+@pytest.mark.parametrize("blocks", [(7, 11), (11, 7), (16, 32), (32, 16), (16, 16)])
+def test_online_tiled_matches_two_pass(T, blocks, causal):
+    shape = (1, 2, T, 8)
+    q, k, v = (_rand(shape, seed=i + 100 * T) for i in range(3))
+    o2, lse2 = oracle.attention_forward(q, k, v, 0.5, causal)
+    o1, lse1 = oracle.attention_forward_online(q, k, v, 0.5, causal, *blocks)
+    np.testing.assert_allclose(o1, o2, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse1, lse2, atol=1e-12, rtol=0)
+
+
+def test_online_tiled_causal_skip_regression_shape():
+    # T=33 with query blocks of 7 and key blocks of 11: skipping one key tile
+    # too many would drop keys of the last rows of a query tile.
+    shape = (1, 1, 33, 4)
+    q, k, v = (_rand(shape, seed=500 + i) for i in range(3))
+    o1, lse1 = oracle.attention_forward_online(q, k, v, 1.0, True, 7, 11)
+    o_t, lse_t = _torch_attention(q, k, v, 1.0, True)
+    np.testing.assert_allclose(o1, o_t, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse1, lse_t, atol=1e-12, rtol=0)
+
+
+def test_online_tiled_rescale_when_max_is_late():
+    # The largest scores sit in the last key tile, so acc must be rescaled.
+    T, D = 40, 4
+    q = np.ones((1, 1, T, D))
+    k = _rand((1, 1, T, D), seed=1) * 0.1
+    k[0, 0, -3:] = 5.0
+    v = _rand((1, 1, T, D), seed=2)
+    o1, lse1 = oracle.attention_forward_online(q, k, v, 1.0, False, 8, 8)
+    o_t, lse_t = _torch_attention(q, k, v, 1.0, False)
+    np.testing.assert_allclose(o1, o_t, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse1, lse_t, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("T", [1, 5, 64, 129])
+def test_uniform_scores_closed_form(T):
+    # Q = 0 makes every visible score equal: O is a mean of V rows and
+    # LSE = ln(number of visible keys).
+    D = 8
+    q = np.zeros((1, 1, T, D))
+    k = _rand((1, 1, T, D), seed=7)
+    v = _rand((1, 1, T, D), seed=8)
+    o, lse = oracle.attention_forward(q, k, v, 0.7, False)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0].mean(axis=0), (T, D)), atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], np.full(T, math.log(T)), atol=1e-13)
+    o, lse = oracle.attention_forward(q, k, v, 0.7, True)
+    prefix = np.cumsum(v[0, 0], axis=0) / np.arange(1, T + 1)[:, None]
+    np.testing.assert_allclose(o[0, 0], prefix, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.arange(1, T + 1)), atol=1e-13)
+    # scale = 0 has the same effect with arbitrary Q
+    q2 = _rand((1, 1, T, D), seed=9)
+    o, lse = oracle.attention_forward(q2, k, v, 0.0, True)
+    np.testing.assert_allclose(o[0, 0], prefix, atol=1e-13)
+
+
+def test_single_key_closed_form():
+    # T = 1: O = V and LSE = scale * q.k
+    q, k, v = (_rand((2, 3, 1, 16), seed=20 + i) for i in range(3))
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, 0.25, causal)
+        np.testing.assert_array_equal(o, v)
+        np.testing.assert_allclose(lse, 0.25 * np.sum(q * k, axis=-1), atol=1e-14)
+
+
+def test_causal_row_zero_is_v0():
+    q, k, v = (_rand((2, 2, 50, 16), seed=30 + i) for i in range(3))
+    o, lse = oracle.attention_forward(q, k, v, 0.25, True)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.25 * np.sum(q[:, :, 0] * k[:, :, 0], axis=-1),
+                               atol=1e-14)
+
+
+def test_two_key_hand_example():
+    # D = 1, T = 2, scale = 1: q = (1, 2), k = (0, 1), v = (3, 5).
+    # Row 0 scores (0, 1): weights (1, e)/(1+e); row 1 scores (0, 2): (1, e^2)/(1+e^2).
+    q = np.array([1.0, 2.0]).reshape(1, 1, 2, 1)
+    k = np.array([0.0, 1.0]).reshape(1, 1, 2, 1)
+    v = np.array([3.0, 5.0]).reshape(1, 1, 2, 1)
+    e = math.e
+    o, lse = oracle.attention_forward(q, k, v, 1.0, False)
+    assert abs(o[0, 0, 0, 0] - (3 + 5 * e) / (1 + e)) < 1e-14
+    assert abs(o[0, 0, 1, 0] - (3 + 5 * e * e) / (1 + e * e)) < 1e-14
+    assert abs(lse[0, 0, 0] - math.log(1 + e)) < 1e-14
+    assert abs(lse[0, 0, 1] - math.log(1 + e * e)) < 1e-14
+    o, lse = oracle.attention_forward(q, k, v, 1.0, True)
+    assert o[0, 0, 0, 0] == 3.0 and lse[0, 0, 0] == 0.0
+    assert abs(o[0, 0, 1, 0] - (3 + 5 * e * e) / (1 + e * e)) < 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    q, k, v = (_rand((1, 2, 70, 8), seed=40 + i) * 3 for i in range(3))
+    _, lse = oracle.attention_forward(q, k, v, 0.5, causal)
+    for h in range(2):
+        s = oracle.scores(q[0, h], k[0, h], 0.5, causal)
+        np.testing.assert_allclose(np.exp(s - lse[0, h][:, None]).sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_spiky_keys_match_torch():
+    # Long-context workload shape in miniature: 1% of key rows scaled by 8.
+    import synth
+    d = synth.make_inputs(1, 2, 301, 16, "bf16", seed=5, spike_frac=0.01)
+    assert len(d["spikes"]) == 3
+    q, k, v = (synth.bf16_bits_to_f64(d[n]) for n in "qkv")
+    o, lse = oracle.attention_forward(q, k, v, 0.25, True)
+    o_t, lse_t = _torch_attention(q, k, v, 0.25, True)
+    np.testing.assert_allclose(o, o_t, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, lse_t, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- backward
+def _loss(q, k, v, do, scale, causal):
+    o, _ = oracle.attention_forward(q, k, v, scale, causal)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 5, 3), (1, 1, 9, 4), (1, 1, 2, 2)])
+def test_backward_matches_finite_differences(shape, causal):
+    q, k, v, do = (_rand(shape, seed=60 + i) for i in range(4))
+    scale = 0.6
+    o, lse = oracle.attention_forward(q, k, v, scale, causal)
+    dq, dk, dv = oracle.attention_backward(q, k, v, o, do, lse, scale, causal)
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(q, k, v, do, scale, causal)
+            x[idx] = old - h
+            lm = _loss(q, k, v, do, scale, causal)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd(causal):
+    shape = (2, 2, 45, 16)
+    q, k, v, do = (_rand(shape, seed=80 + i) for i in range(4))
+    scale = 0.25
+    o, lse = oracle.attention_forward(q, k, v, scale, causal)
+    dq, dk, dv = oracle.attention_backward(q, k, v, o, do, lse, scale, causal)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    to = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def test_backward_delta_identity():
+    # sum_j P_ij dP_ij == rowsum(dO * O)  (Lab 06 section 4)
+    shape = (1, 1, 33, 8)
+    q, k, v, do = (_rand(shape, seed=95 + i) for i in range(4))
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, 0.4, causal)
+        s = oracle.scores(q[0, 0], k[0, 0], 0.4, causal)
+        p = np.exp(s - lse[0, 0][:, None])
+        dp = do[0, 0] @ v[0, 0].T
+        np.testing.assert_allclose(np.sum(p * dp, axis=1), oracle.backward_delta(o, do)[0, 0],
+                                   atol=1e-12)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _forward_pins_pass():
+    shape = (1, 2, 33, 8)
+    q, k, v = (_rand(shape, seed=200 + i) for i in range(3))
+    ok = True
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, 0.3, causal)
+        o_t, lse_t = _torch_attention(q, k, v, 0.3, causal)
+        ok &= np.allclose(o, o_t, atol=1e-10, rtol=0) and np.allclose(lse, lse_t, atol=1e-10, rtol=0)
+    return ok
+
+
+def test_planted_forward_mistakes_are_caught(monkeypatch):
+    assert _forward_pins_pass()
+    real_scores = oattn.scores
+
+    def flipped_mask(q_bh, k_bh, scale, causal, rows=None):
+        s = real_scores(q_bh, k_bh, scale, False, rows)
+        if causal:
+            r = np.arange(q_bh.shape[0]) if rows is None else rows
+            s = np.where(np.arange(k_bh.shape[0])[None, :] >= r[:, None], s, -np.inf)
+        return s
+
+    def dropped_scale(q_bh, k_bh, scale, causal, rows=None):
+        return real_scores(q_bh, k_bh, 1.0, causal, rows)
+
+    def off_by_one_mask(q_bh, k_bh, scale, causal, rows=None):
+        s = real_scores(q_bh, k_bh, scale, False, rows)
+        if causal:
+            r = np.arange(q_bh.shape[0]) if rows is None else rows
+            s = np.where(np.arange(k_bh.shape[0])[None, :] < r[:, None], s, -np.inf)
+            s[:, 0] = np.where(np.isneginf(s[:, 0]), 0.0, s[:, 0])
+        return s
+
+    for bad in (flipped_mask, dropped_scale, off_by_one_mask):
+        monkeypatch.setattr(oattn, "scores", bad)
+        assert not _forward_pins_pass(), bad.__name__
+        monkeypatch.setattr(oattn, "scores", real_scores)
+
+    real_stats = oattn.softmax_stats
+
+    def log2_lse(s):
+        m, l, _ = real_stats(s)
+        return m, l, m + np.log2(l)
+
+    monkeypatch.setattr(oattn, "softmax_stats", log2_lse)
+    assert not _forward_pins_pass()
+
+
+def test_planted_backward_mistakes_are_caught(monkeypatch):
+    shape = (1, 1, 6, 3)
+    q, k, v, do = (_rand(shape, seed=300 + i) for i in range(4))
+    scale = 0.6
+
+    def fd_ok():
+        o, lse = oracle.attention_forward(q, k, v, scale, True)
+        grads = oracle.attention_backward(q, k, v, o, do, lse, scale, True)
+        h = 1e-6
+        for x, g in zip((q, k, v), grads):
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp = _loss(q, k, v, do, scale, True)
+                x[idx] = old - h
+                lm = _loss(q, k, v, do, scale, True)
+                x[idx] = old
+                if abs((lp - lm) / (2 * h) - g[idx]) > 1e-6 * max(1.0, abs(g[idx])):
+                    return False
+        return True
+
+    assert fd_ok()
+
+    # forgetting the mask in the backward: recompute P from unmasked scores
+    real_scores = oattn.scores
+    # (the backward asks for all rows at once; the forward passes row indices)
+    monkeypatch.setattr(oattn, "scores",
+                        lambda qb, kb, sc, causal, rows=None:
+                        real_scores(qb, kb, sc, causal and rows is not None, rows))
+    ok = fd_ok()
+    monkeypatch.setattr(oattn, "scores", real_scores)
+    assert not ok
+
+    # dropping D from dS = P * (dP - D)
+    real_bwd = oattn.attention_backward
+
+    def no_delta(q_, k_, v_, o_, do_, lse_, sc, causal):
+        return real_bwd(q_, k_, v_, np.zeros_like(o_), do_, lse_, sc, causal)
+
+    monkeypatch.setattr(oattn, "attention_backward", no_delta)
+    monkeypatch.setattr(oracle, "attention_backward", no_delta)
+    ok = fd_ok()
+    monkeypatch.setattr(oattn, "attention_backward", real_bwd)
+    monkeypatch.setattr(oracle, "attention_backward", real_bwd)
+    assert not ok
