@@ -1,0 +1,176 @@
+"""Benchmark: attention forward TFLOP/s on one MI355X, and % of the bf16 MFMA peak.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one forward pass (fa_fwd: one kernel launch) over the headline
+workload: causal bf16, B=4, H=16, T=4096, D=128, scale 1/sqrt(128), seeded
+N(0,1) inputs already resident in HBM. FLOPs per step = 4*B*H*T^2*D / 2.
+The backward (fa_bwd, three kernels) is measured the same way on its own
+workload (causal bf16, B=2, H=16, T=4096, D=128) and reported under
+"backward". The CPU baseline times the float64 oracle on a bounded sample of
+the forward workload (whole (b, h) heads) on the host cores.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FWD_WORKLOAD = "fwd_bf16_b4h16t4096d128_causal"
+BWD_WORKLOAD = "bwd_bf16_b2h16t4096d128_causal"
+
+
+def _dev(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def _time_launches(torch, fn, steps, warmup):
+    """Warm up, then time `steps` calls of fn() with one event pair per call on the
+    current stream (where fn enqueues its kernels). Returns (total_ms, per_call_ms)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in ev]
+    total = ev[0][0].elapsed_time(ev[-1][1])
+    return total, per, wall_ms
+
+
+def cpu_baseline(w, d, budget_s: float):
+    """Time the float64 oracle on whole (b, h) heads of the same inputs, in order,
+    until budget_s has passed."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        b, h = divmod(heads, w.H)
+        q, k, v = (synth.bf16_bits_to_f64(d[n][b:b + 1, h:h + 1]) for n in "qkv")
+        oracle.attention_forward(q, k, v, w.scale, w.causal)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or heads >= w.B * w.H:
+            break
+    flops = 4.0 * heads * w.T * w.T * w.D / (2.0 if w.causal else 1.0)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (b,h) heads of B={w.B} H={w.H} T={w.T} D={w.D} "
+                      f"{'causal' if w.causal else 'non-causal'}; float64, full S materialised; "
+                      f"{el:.1f} s", "seconds": el}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_flash_amd as fa
+    import synth
+    from exact_tiled_attention_flash_amd import metrics
+
+    w = synth.WORKLOADS[FWD_WORKLOAD]
+    d = synth.make_workload_inputs(w, seed=0)
+    q, k, v = (_dev(d[n], torch) for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    total_ms, per, wall_ms = _time_launches(torch, step, args.steps, args.warmup)
+    flops = metrics.fwd_flops(w.B, w.H, w.T, w.D, w.causal)
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = float(np.mean(per))
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = metrics.PEAK_TFLOPS["bf16"]
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    out = {
+        "metric": "attention fwd TFLOP/s (4*B*H*T^2*D, causal halved) and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), numpy PCG64 seed 0, RNE to bf16)",
+        "config": {"workload": FWD_WORKLOAD, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
+                   "causal": w.causal, "scale": w.scale},
+        "pct_of_bf16_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "fwd_bf16_kernel<128, causal>",
+                     "avg_launch_ms": round(avg_launch_ms, 5),
+                     "min_launch_ms": round(float(np.min(per)), 5),
+                     "median_launch_ms": round(float(np.median(per)), 5),
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": metrics.fwd_bytes(w.B, w.H, w.T, w.D, 2)},
+        "wall_ms_timed_region": round(wall_ms, 3),
+    }
+
+    lib = fa.load_library()
+    if not args.no_backward and hasattr(lib, "fa_bwd"):
+        wb = synth.WORKLOADS[BWD_WORKLOAD]
+        db = synth.make_workload_inputs(wb, seed=0)
+        bq, bk, bv, bdo = (_dev(db[n], torch) for n in ("q", "k", "v", "do"))
+        bo, blse = fa.fa_fwd(bq, bk, bv, causal=wb.causal, scale=wb.scale)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(wb.B, wb.H, wb.T, wb.D), dtype=torch.uint8,
+                         device="cuda")
+
+        def bstep():
+            fa.fa_bwd(bq, bk, bv, bo, bdo, blse, causal=wb.causal, scale=wb.scale, workspace=ws)
+
+        btotal, bper, _ = _time_launches(torch, bstep, max(5, args.steps // 2), args.warmup)
+        bflops = metrics.bwd_flops(wb.B, wb.H, wb.T, wb.D, wb.causal)
+        bms = btotal / max(5, args.steps // 2)
+        out["backward"] = {"workload": BWD_WORKLOAD, "ms_per_step": round(bms, 5),
+                           "tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
+                           "flops_per_step": bflops,
+                           "flop_count": "10*B*H*T^2*D/2 (S recompute, dP, dV, dQ, dK)",
+                           "pct_of_bf16_peak": round(100.0 * bflops / (bms * 1e-3) / 1e12 / peak, 2)}
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, d, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,5 +1,21 @@
 """MI355X-native exact tiled attention (FlashAttention forward and backward).
 
 The compute lives in hand-written HIP kernels for gfx950 behind the C ABI
-declared in include/fa.h (libfa.so); this package is a thin binding over it.
+declared in include/fa.h (libfa.so); this package is a thin ctypes binding
+over it with the same entry-point names. Importing it loads libfa.so and
+fails loudly if the library has not been built.
 """
+from ._lib import (  # noqa: F401
+    FA_BF16,
+    FA_F32,
+    FaError,
+    LIB_PATH,
+    fa_abi_version,
+    fa_bwd,
+    fa_bwd_workspace_bytes,
+    fa_fwd,
+    fa_status_string,
+    load_library,
+)
+
+load_library()

@@ -1,0 +1,147 @@
+"""ctypes binding to libfa.so: argument marshalling only.
+
+Every step of the attention computation runs in the HIP kernels behind the C
+ABI (include/fa.h). torch supplies device memory and the current stream. If
+the library is missing the import fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F32 = 0
+FA_BF16 = 1
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_HEADDIM = -3
+FA_ERR_DTYPE = -4
+FA_ERR_ALIGN = -5
+FA_ERR_SCALE = -6
+FA_ERR_ARG = -7
+FA_ERR_HIP = -8
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m exact_tiled_attention_flash_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_abi_version.restype = i
+    lib.fa_abi_version.argtypes = []
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    if hasattr(lib, "fa_bwd"):
+        lib.fa_bwd.restype = i
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                               i, i, i, i, f, i, i, vp]
+        lib.fa_bwd_workspace_bytes.restype = sz
+        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    _lib = lib
+    return lib
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libfa status {status}: {fa_status_string(status)}")
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check(name: str, t: torch.Tensor, like: torch.Tensor | None = None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (B, H, T, D)")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype
+                             or t.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+           scale: float | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None):
+    """o, lse = softmax(scale q k^T [causal]) v, per-row log-sum-exp. Enqueued on the
+    current stream. q, k, v: contiguous (B, H, T, D) bf16 or fp32 device tensors."""
+    lib = load_library()
+    _check("q", q)
+    _check("k", k, q)
+    _check("v", v, q)
+    if q.dim() != 4:
+        raise ValueError("q must be (B, H, T, D)")
+    B, H, T, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("out", o, q)
+    if l.dtype != torch.float32 or tuple(l.shape) != (B, H, T) or not l.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, T) tensor")
+    rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                    B, H, T, D, float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, l
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, T: int, D: int) -> int:
+    return load_library().fa_bwd_workspace_bytes(B, H, T, D)
+
+
+def fa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+           workspace: torch.Tensor | None = None):
+    """dq, dk, dv of L with dL/do = dout, from the forward's o and lse. Enqueued on the
+    current stream."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(name, t, None if name == "q" else q)
+    B, H, T, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, T) tensor")
+    need = fa_bwd_workspace_bytes(B, H, T, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                    B, H, T, D, float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return dq, dk, dv

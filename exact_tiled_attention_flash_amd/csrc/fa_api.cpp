@@ -1,0 +1,72 @@
+// C ABI of libfa.so: argument validation and kernel dispatch (declared in include/fa.h).
+//
+// Every check runs on the host before anything is enqueued, so a rejected
+// call leaves all outputs untouched and makes no HIP runtime call at all.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;   // per tensor; keeps every offset in range
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_sizes(int B, int H, int T, int D) {
+  if (B < 1 || H < 1 || T < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+  const int64_t bh = int64_t(B) * H;
+  if (bh > INT32_MAX) return FA_ERR_SHAPE;
+  if (bh * T * D > kMaxElems) return FA_ERR_SHAPE;
+  // the largest grid: one workgroup per 64 rows of every (b, h)
+  if (bh * ((int64_t(T) + 63) / 64) > kMaxBlocks) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) {
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, T must be >= 1 and sizes must fit the index range)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (D must be 64 or 128)";
+    case FA_ERR_DTYPE: return "unsupported dtype for this call";
+    case FA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_ARG: return "invalid argument";
+    case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+           int D, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (int rc = check_sizes(B, H, T, D)) return rc;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, T, D, scale, causal != 0,
+                static_cast<hipStream_t>(stream)};
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

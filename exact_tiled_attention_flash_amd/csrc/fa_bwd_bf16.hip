@@ -1,0 +1,394 @@
+// Attention backward, bf16 storage, fp32 accumulation: three hand-written gfx950 kernels.
+//
+// Method: "Lab 06 - Attention kernels", section 4: with P = exp(S - LSE)
+// recomputed per tile from the saved LSE, dV = P^T dO, dP = dO V^T,
+// dS = P * (dP - D) where D_i = rowsum(dO * O)_i (an O(T d) pass instead of
+// a reduction over P), dQ = dS K scale and dK = dS^T Q scale; the causal
+// mask is applied before the exponential exactly as in the forward ("Common
+// bugs"). Work split per the page's "Stretch" list: one kernel with key
+// tiles outer (dK, dV accumulate in registers) and one with query tiles
+// outer (dQ accumulates in registers), so no atomics are needed and the
+// result is deterministic.
+//
+//   bwd_pre_kernel   D_i = sum_d dO_id O_id                      (HBM-bound)
+//   bwd_dkdv_kernel  workgroup = 128 keys (32 per wave) of one (b, h); loops
+//                    over 64-query tiles from the diagonal down. Per wave:
+//                    S = Q K^T and dP = dO V^T with K, V held in registers
+//                    (lane = key), then dV^T += dO^T P and dK^T += Q^T dS,
+//                    whose A operands come from transposed Q / dO tiles in LDS.
+//   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key
+//                    tiles up to the diagonal. Per wave: S^T = K Q^T and
+//                    dP^T = V dO^T with Q, dO in registers (lane = query),
+//                    then dQ^T += K^T dS^T from a transposed K tile in LDS.
+// The accumulator layout of S / S^T doubles as the B-operand layout of the
+// following product (k-slots permuted the same way for both operands), so P
+// and dS never leave registers.
+
+#include "fa_common.h"
+#include "fa_launch.h"
+#include "fa_tile.h"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kPosInf = __builtin_inff();
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// ------------------------------------------------------------------ D_i = rowsum(dO * O)
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __restrict__ O,
+                                                           const uint16_t* __restrict__ dO,
+                                                           float* __restrict__ Dv, int64_t rows) {
+  constexpr int LPR = D / 8;             // lanes per row, one 16-byte chunk each
+  constexpr int RPB = kThreads / LPR;    // rows per workgroup
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int ch = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + ch * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + ch * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (ch == 0 && row < rows) Dv[row] = s;
+}
+
+// Store a 32 x D block held as D/32 accumulators (lane = row, registers = d).
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(uint16_t* __restrict__ dst, const f32x16 (&acc)[D / 32],
+                                                float mul, int h) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w = {pack_bf16x2(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                 pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * g + 4 * h) = w;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+constexpr int kKeysPerWG = 128;
+constexpr int kQTile = 64;
+
+template <int D>
+struct DkdvSmem {
+  static constexpr int rPitch = D + 8;        // row-major copies (bf16 elements)
+  static constexpr int cPitch = kQTile + 4;   // transposed copies
+  static constexpr int qRows = 0;
+  static constexpr int qCols = qRows + kQTile * rPitch;
+  static constexpr int doRows = qCols + D * cPitch;
+  static constexpr int doCols = doRows + kQTile * rPitch;
+  static constexpr int bf16Elems = doCols + D * cPitch;
+  static constexpr int stageBytes = bf16Elems * 2 + 2 * kQTile * 4;  // + lse2[64], dvec[64]
+  static_assert(stageBytes % 16 == 0, "stage alignment");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, float c, float scale) {
+  using Sm = DkdvSmem<D>;
+  using Tile = RowTile<D>;
+  constexpr int nD = D / 32;
+  constexpr int nK = D / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Sm::stageBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int L = blockIdx.x;
+  const int bh = L % BH;
+  const int k0 = (L / BH) * kKeysPerWG;   // key tile 0 (the heaviest when causal) first
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  const size_t base = (size_t)bh * T * D;
+
+  bf16x8 kf[nK], vf[nK];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) {
+    const size_t off = base + (size_t)key * D + kk * 16 + h * 8;
+    kf[kk] = as_bf16x8(key < T ? *reinterpret_cast<const u32x4*>(K + off) : u32x4{0u, 0u, 0u, 0u});
+    vf[kk] = as_bf16x8(key < T ? *reinterpret_cast<const u32x4*>(V + off) : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  f32x16 dk[nD], dv[nD];
+#pragma unroll
+  for (int db = 0; db < nD; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const int nqt = (T + kQTile - 1) / kQTile;
+  const int qt0 = CAUSAL ? k0 / kQTile : 0;
+
+  u32x4 qr[Tile::RPT], dor[Tile::RPT];
+  float stat = 0.f;  // thread t < 64: lse2 of query t; 64 <= t < 128: D of query t - 64
+  auto fetch = [&](int qt) {
+    const int q0 = qt * kQTile;
+    Tile::load(Q + base, q0, T, tid, qr);
+    Tile::load(dO + base, q0, T, tid, dor);
+    if (tid < 2 * kQTile) {
+      const int q = q0 + (tid & (kQTile - 1));
+      if (tid < kQTile) stat = q < T ? LSE[(size_t)bh * T + q] * kLog2e : kPosInf;
+      else stat = q < T ? Dv[(size_t)bh * T + q] : 0.f;
+    }
+  };
+  auto stash = [&](uint8_t* st) {
+    uint16_t* b = reinterpret_cast<uint16_t*>(st);
+    Tile::store_rows(b + Sm::qRows, Sm::rPitch, tid, qr);
+    Tile::store_cols(b + Sm::qCols, Sm::cPitch, tid, qr);
+    Tile::store_rows(b + Sm::doRows, Sm::rPitch, tid, dor);
+    Tile::store_cols(b + Sm::doCols, Sm::cPitch, tid, dor);
+    if (tid < 2 * kQTile) reinterpret_cast<float*>(st + Sm::bf16Elems * 2)[tid] = stat;
+  };
+
+  fetch(qt0);
+  stash(smem);
+  __syncthreads();
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int it = qt - qt0;
+    const bool more = qt + 1 < nqt;
+    if (more) fetch(qt + 1);
+    const uint8_t* st = smem + (it & 1) * Sm::stageBytes;
+    const uint16_t* sb = reinterpret_cast<const uint16_t*>(st);
+    const float* lse2 = reinterpret_cast<const float*>(st + Sm::bf16Elems * 2);
+    const float* dvec = lse2 + kQTile;
+    const int q0 = qt * kQTile;
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qb0 = q0 + qb * 32;
+      if (CAUSAL && qb0 + 31 < kw0) continue;  // every query of the block precedes every key
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < nK; ++kk) {
+        const int off = (qb * 32 + l32) * Sm::rPitch + kk * 16 + h * 8;
+        s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(sb + Sm::qRows + off)), kf[kk], s);
+        dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(sb + Sm::doRows + off)), vf[kk], dp);
+      }
+      // lane = key; register r = query qb0 + 8*(r/4) + 4h + (r%4)
+      const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (kw0 + 32 > T);
+      f32x16 p, ds;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qb * 32 + 8 * g + 4 * h);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvec + qb * 32 + 8 * g + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          float pv = exp2_fast(fmaf(s[r], c, -l4[i]));
+          if (need_mask) {
+            const int qi = qb0 + 8 * g + 4 * h + i;
+            const bool ok = key < T && (!CAUSAL || key <= qi);
+            pv = ok ? pv : 0.f;
+          }
+          p[r] = pv;
+          ds[r] = pv * (dp[r] - d4[i]);
+        }
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int o = cc * 8;
+        pb[cc] = as_bf16x8(u32x4{pack_bf16x2(p[o], p[o + 1]), pack_bf16x2(p[o + 2], p[o + 3]),
+                                 pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7])});
+        dsb[cc] = as_bf16x8(u32x4{pack_bf16x2(ds[o], ds[o + 1]), pack_bf16x2(ds[o + 2], ds[o + 3]),
+                                  pack_bf16x2(ds[o + 4], ds[o + 5]), pack_bf16x2(ds[o + 6], ds[o + 7])});
+      }
+#pragma unroll
+      for (int db = 0; db < nD; ++db) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int crow = db * 32 + l32;
+          dv[db] = mfma32(load_perm_k(sb + Sm::doCols, Sm::cPitch, crow, qb * 32 + 16 * cc, h), pb[cc], dv[db]);
+          dk[db] = mfma32(load_perm_k(sb + Sm::qCols, Sm::cPitch, crow, qb * 32 + 16 * cc, h), dsb[cc], dk[db]);
+        }
+      }
+    }
+    if (more) stash(smem + ((it + 1) & 1) * Sm::stageBytes);
+    __syncthreads();
+  }
+
+  if (key < T) {
+    store_rows_bf16<D>(dV + base + (size_t)key * D, dv, 1.0f, h);
+    store_rows_bf16<D>(dK + base + (size_t)key * D, dk, scale, h);
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+constexpr int kQueriesPerWG = 128;
+constexpr int kKTile = 64;
+
+template <int D>
+struct DqSmem {
+  static constexpr int rPitch = D + 8;
+  static constexpr int cPitch = kKTile + 4;
+  static constexpr int kRows = 0;
+  static constexpr int vRows = kRows + kKTile * rPitch;
+  static constexpr int kCols = vRows + kKTile * rPitch;
+  static constexpr int stageElems = kCols + D * cPitch;
+  static_assert((stageElems * 2) % 16 == 0, "stage alignment");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dQ, int T, int BH, int nq, float c, float scale) {
+  using Sm = DqSmem<D>;
+  using Tile = RowTile<D>;
+  constexpr int nD = D / 32;
+  constexpr int nK = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Sm::stageElems];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const int L = blockIdx.x;
+  const int bh = L % BH;
+  int qt = L / BH;
+  if (CAUSAL) qt = nq - 1 - qt;  // longest key range first
+  const int q0 = qt * kQueriesPerWG;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  const size_t base = (size_t)bh * T * D;
+
+  bf16x8 qf[nK], dof[nK];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) {
+    const size_t off = base + (size_t)qrow * D + kk * 16 + h * 8;
+    qf[kk] = as_bf16x8(qrow < T ? *reinterpret_cast<const u32x4*>(Q + off) : u32x4{0u, 0u, 0u, 0u});
+    dof[kk] = as_bf16x8(qrow < T ? *reinterpret_cast<const u32x4*>(dO + off) : u32x4{0u, 0u, 0u, 0u});
+  }
+  const float lse2 = qrow < T ? LSE[(size_t)bh * T + qrow] * kLog2e : kPosInf;
+  const float dval = qrow < T ? Dv[(size_t)bh * T + qrow] : 0.f;
+
+  f32x16 dq[nD];
+#pragma unroll
+  for (int db = 0; db < nD; ++db) dq[db] = f32x16{};
+
+  const int kend = CAUSAL ? min(T, q0 + kQueriesPerWG) : T;
+  const int ntiles = (kend + kKTile - 1) / kKTile;
+
+  u32x4 kr[Tile::RPT], vr[Tile::RPT];
+  auto stash = [&](uint16_t* st) {
+    Tile::store_rows(st + Sm::kRows, Sm::rPitch, tid, kr);
+    Tile::store_cols(st + Sm::kCols, Sm::cPitch, tid, kr);
+    Tile::store_rows(st + Sm::vRows, Sm::rPitch, tid, vr);
+  };
+  Tile::load(K + base, 0, T, tid, kr);
+  Tile::load(V + base, 0, T, tid, vr);
+  stash(smem);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * kKTile;
+    const bool more = j + 1 < ntiles;
+    if (more) {
+      Tile::load(K + base, k0 + kKTile, T, tid, kr);
+      Tile::load(V + base, k0 + kKTile, T, tid, vr);
+    }
+    const uint16_t* st = smem + (j & 1) * Sm::stageElems;
+    if (!(CAUSAL && k0 > qw0 + 31)) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < nK; ++kk) {
+          const int off = (kb * 32 + l32) * Sm::rPitch + kk * 16 + h * 8;
+          s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(st + Sm::kRows + off)), qf[kk], s[kb]);
+          dp[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(st + Sm::vRows + off)), dof[kk], dp[kb]);
+        }
+      }
+      // lane = query; register r of block kb = key k0 + 32 kb + 8*(r/4) + 4h + (r%4)
+      const bool need_mask = (k0 + kKTile > T) || (CAUSAL && (k0 + kKTile - 1 > qw0));
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = exp2_fast(fmaf(s[kb][r], c, -lse2));
+          if (need_mask) {
+            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool ok = kj < T && (!CAUSAL || kj <= qrow);
+            pv = ok ? pv : 0.f;
+          }
+          ds[r] = pv * (dp[kb][r] - dval);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int o = half * 8;
+          dsb[2 * kb + half] =
+              as_bf16x8(u32x4{pack_bf16x2(ds[o], ds[o + 1]), pack_bf16x2(ds[o + 2], ds[o + 3]),
+                              pack_bf16x2(ds[o + 4], ds[o + 5]), pack_bf16x2(ds[o + 6], ds[o + 7])});
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < nD; ++db) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          dq[db] = mfma32(load_perm_k(st + Sm::kCols, Sm::cPitch, db * 32 + l32, 16 * cc, h), dsb[cc], dq[db]);
+      }
+    }
+    if (more) stash(smem + ((j + 1) & 1) * Sm::stageElems);
+    __syncthreads();
+  }
+
+  if (qrow < T) store_rows_bf16<D>(dQ + base + (size_t)qrow * D, dq, scale, h);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& a) {
+  const int BH = a.B * a.H;
+  const float c = a.scale * kLog2e;
+  const int64_t rows = (int64_t)BH * a.T;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  const uint16_t* o = static_cast<const uint16_t*>(a.o);
+  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+  constexpr int rpb = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kThreads),
+                     0, a.stream, o, dout, a.delta, rows);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int nk = (a.T + kKeysPerWG - 1) / kKeysPerWG;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nk * BH), dim3(kThreads), 0, a.stream, q, k,
+                     v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk),
+                     static_cast<uint16_t*>(a.dv), a.T, BH, c, a.scale);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int nq = (a.T + kQueriesPerWG - 1) / kQueriesPerWG;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream, q, k,
+                     v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), a.T, BH, nq, c,
+                     a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  if (a.D == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,97 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact tiled attention library, libfa.so.
+ *
+ * The operation is exact softmax attention,
+ *     S = scale * Q K^T,   P = softmax_rows(S),   O = P V,
+ *     LSE_i = log sum_j exp(S_ij)           (natural log, one value per row),
+ * computed by the online-softmax tile recurrence so the T x T matrix never
+ * reaches device memory, and its gradient computed from the saved LSE with
+ * D_i = rowsum(dO * O) and per-tile recomputation of P.
+ * Sources:
+ *   "Lab 06 - Attention kernels: online softmax -> FlashAttention -> Triton",
+ *     section 2 (online softmax), section 3 (forward recurrence, causal tile
+ *     skipping, O = acc / l and LSE = m + log l), section 4 (backward with
+ *     D = rowsum(dO * O), dQ = dS K scale, dK = dS^T Q scale), section 5
+ *     (one program per (query tile, batch*head); contiguous (B, H, T, D)).
+ *   "Triton FlashAttention-2 forward", "The kernel" (launcher layout, scale
+ *     1/sqrt(D) by default, fp32 accumulation, output cast to input dtype).
+ *   "Flash Attention and Kernel Optimization", "Output and saved state" (the
+ *     saved LSE row statistic used by the backward).
+ *
+ * Conventions shared by every call
+ *   Layout     q, k, v, o, dout, dq, dk, dv are contiguous row-major
+ *              (B, H, T, D) arrays: element (b, h, t, d) sits at
+ *              ((b*H + h)*T + t)*D + d. lse and the backward workspace hold
+ *              (B, H, T) float32 values at (b*H + h)*T + t.
+ *   Types      dtype FA_BF16: tensors hold bfloat16 (products in bf16 on the
+ *              matrix cores, accumulation and all softmax statistics in fp32,
+ *              outputs rounded to nearest-even). dtype FA_F32: everything is
+ *              IEEE fp32. lse is always float32.
+ *   Masking    causal != 0: key j is visible to query i iff j <= i; one
+ *              length T shared by queries and keys.
+ *   Scale      finite and >= 0 (0 gives uniform weights over visible keys);
+ *              callers usually pass 1/sqrt(D).
+ *   Memory     every pointer is device memory owned by the caller and must be
+ *              16-byte aligned. The library never allocates, frees or
+ *              synchronises: each call validates its arguments on the host,
+ *              enqueues kernels on `stream` (a hipStream_t; NULL = the null
+ *              stream) and returns. Results are ready when the stream is.
+ *   Errors     calls return FA_OK (0) or a negative fa_status. On any
+ *              validation error nothing is enqueued and no output is
+ *              touched. FA_ERR_HIP means a kernel launch was rejected by the
+ *              runtime; outputs are then unspecified.
+ *   Threads    calls are reentrant; concurrent calls on different streams
+ *              must not share output buffers.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+enum fa_dtype {
+    FA_F32 = 0,
+    FA_BF16 = 1
+};
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,      /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,     /* B, H or T < 1, or the sizes overflow the index range */
+    FA_ERR_HEADDIM = -3,   /* D is not 64 or 128 */
+    FA_ERR_DTYPE = -4,     /* dtype is not a supported fa_dtype for this call */
+    FA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+    FA_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
+    FA_ERR_ARG = -7,       /* any other bad argument (causal not 0/1, workspace too small) */
+    FA_ERR_HIP = -8        /* the HIP runtime rejected a launch */
+};
+
+/* Version of this ABI (FA_ABI_VERSION). */
+int fa_abi_version(void);
+
+/* Static text for a status code ("ok", "null pointer", ...). Never NULL. */
+const char *fa_status_string(int status);
+
+/*
+ * Forward: o = softmax(scale * q k^T [causal mask]) v and lse per row.
+ *   q, k, v  in:  (B, H, T, D) of dtype
+ *   o        out: (B, H, T, D) of dtype
+ *   lse      out: (B, H, T) float32, natural-log log-sum-exp of each row of
+ *                 scale * q k^T over the visible keys
+ * Source: "Lab 06 - Attention kernels", section 3 (the (m, l, acc)
+ * recurrence; O = acc / l; LSE = m + log l) and section 5 (launch layout).
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int T, int D, float scale, int causal, int dtype,
+           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

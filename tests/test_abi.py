@@ -1,0 +1,93 @@
+"""The C ABI on the host: libfa.so loads, exports every function include/fa.h
+declares, and rejects bad arguments before touching the GPU (no compute calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_tiled_attention_flash_amd as fa
+    return fa.load_library()
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert {"fa_fwd", "fa_status_string", "fa_abi_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from exact_tiled_attention_flash_amd import LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version(lib):
+    assert lib.fa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(-8, 1):
+        assert lib.fa_status_string(code)
+    assert lib.fa_status_string(0) == b"ok"
+    assert lib.fa_status_string(-99) == b"unknown status"
+
+
+# Fake, 16-byte aligned, never dereferenced: every call below fails validation
+# before anything is enqueued.
+P = 4096
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, T=16, D=64, scale=0.125, causal=0, dtype=1):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, T, D, ctypes.c_float(scale), causal, dtype, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointers(lib, which):
+    assert fwd(lib, **{which: None}) == -1
+
+
+@pytest.mark.parametrize("B,H,T", [(0, 1, 16), (1, 0, 16), (1, 1, 0), (-1, 1, 16),
+                                   (1 << 20, 1 << 11, 1 << 20)])
+def test_bad_shapes(lib, B, H, T):
+    assert fwd(lib, B=B, H=H, T=T) == -2
+
+
+@pytest.mark.parametrize("D", [0, 32, 96, 256, 127])
+def test_bad_head_dim(lib, D):
+    assert fwd(lib, D=D) == -3
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_bad_dtype(lib, dtype):
+    assert fwd(lib, dtype=dtype) == -4
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_misaligned(lib, which):
+    assert fwd(lib, **{which: P + 8}) == -5
+
+
+@pytest.mark.parametrize("scale", [-0.5, float("nan"), float("inf")])
+def test_bad_scale(lib, scale):
+    assert fwd(lib, scale=scale) == -6
+
+
+def test_bad_causal(lib):
+    assert fwd(lib, causal=2) == -7
