@@ -69,4 +69,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int T, int D) {
+  if (check_sizes(B, H, T, D) != FA_OK) return 0;
+  return sizeof(float) * size_t(B) * size_t(H) * size_t(T);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+           int B, int H, int T, int D, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (int rc = check_sizes(B, H, T, D)) return rc;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, T, D)) return FA_ERR_ARG;
+  for (const void* p : {q, k, v, o, dout, static_cast<const void*>(lse), static_cast<const void*>(dq),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv), static_cast<const void*>(workspace)})
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), B, H, T, D,
+                scale, causal != 0, static_cast<hipStream_t>(stream)};
+  return fa::launch_bwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

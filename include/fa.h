@@ -90,6 +90,35 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int T, int D, float scale, int causal, int dtype,
            void *stream);
 
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (the D_i row
+ * vector: 4*B*H*T bytes). Returns 0 if the sizes are invalid.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int T, int D);
+
+/*
+ * Backward: given dout = dL/do, compute dq, dk, dv.
+ *   q, k, v, o  in:  as passed to / returned by fa_fwd (o must be that
+ *                    forward's output for the same q, k, v, scale, causal)
+ *   dout        in:  (B, H, T, D) of dtype
+ *   lse         in:  (B, H, T) float32 from that fa_fwd call
+ *   dq, dk, dv  out: (B, H, T, D) of dtype
+ *   workspace   scratch of at least fa_bwd_workspace_bytes(B, H, T, D)
+ *               bytes, owned by the caller; contents on return unspecified
+ * Kernels: D_i = rowsum(dout * o); then dk, dv with key tiles outer and
+ * query tiles inner; then dq with query tiles outer; P = exp(S - LSE) is
+ * recomputed per tile with the same mask as the forward. No atomics: the
+ * result is deterministic. Only dtype FA_BF16 is supported.
+ * Source: "Lab 06 - Attention kernels", section 4 and the "Stretch" list
+ * (two backward kernels: dK/dV with key tiles outer, dQ with query tiles
+ * outer).
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *lse, void *dq, void *dk, void *dv,
+           void *workspace, size_t workspace_bytes,
+           int B, int H, int T, int D, float scale, int causal, int dtype,
+           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,3 +91,25 @@ def test_bad_scale(lib, scale):
 
 def test_bad_causal(lib):
     assert fwd(lib, causal=2) == -7
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 4 * 2 * 16 * 4096
+    assert lib.fa_bwd_workspace_bytes(0, 16, 4096, 128) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 16, 96) == 0
+
+
+def bwd(lib, ws_bytes=1 << 20, dtype=1, D=64, T=16, causal=1, scale=0.1, nulls=()):
+    ptrs = [None if i in nulls else P for i in range(10)]
+    return lib.fa_bwd(*ptrs, ws_bytes, 1, 1, T, D, ctypes.c_float(scale), causal, dtype, None)
+
+
+def test_bwd_validation(lib):
+    for i in range(10):
+        assert bwd(lib, nulls=(i,)) == -1
+    assert bwd(lib, T=0) == -2
+    assert bwd(lib, D=32) == -3
+    assert bwd(lib, dtype=0) == -4      # the backward is bf16 only
+    assert bwd(lib, scale=-1.0) == -6
+    assert bwd(lib, causal=5) == -7
+    assert bwd(lib, ws_bytes=63) == -7  # needs 4*B*H*T = 64 bytes

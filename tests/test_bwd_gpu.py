@@ -1,0 +1,142 @@
+"""Backward parity on the GPU: fa_bwd (through the C ABI) against the CPU float64
+oracle's backward. The GPU backward takes O and LSE from the GPU forward; the
+oracle uses its own float64 forward.
+
+Tolerance: max-abs <= 2e-2 on dQ, dK, dV for bf16 inputs. Outputs are stored in
+bf16, so an entry of magnitude >= 8 cannot be closer than half a bf16 ulp
+(0.03125) to the exact value; such entries are allowed that rounding floor
+on top of 2e-2 and the test reports how many there were.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import as_f64, device_tensor, host_f64
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_tiled_attention_flash_amd as m
+    return m
+
+
+def _half_ulp_bf16(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 2.0 ** (e - 8)  # bf16 has 8 significant bits (7 stored)
+
+
+def _check_grad(g, ref, name):
+    err = np.abs(g - ref)
+    assert np.all(np.isfinite(g)), name
+    floor = np.where(np.abs(ref) >= 8.0, _half_ulp_bf16(ref), 0.0)
+    bad = err > TOL + floor
+    assert not bad.any(), (f"{name}: max-abs {err.max():.3e} at |ref| "
+                           f"{np.abs(ref).ravel()[err.argmax()]:.3f}; {bad.sum()} over tolerance")
+    return float(err.max()), int((np.abs(ref) >= 8.0).sum())
+
+
+def _gpu_fwd_bwd(fa, d, causal, scale):
+    q, k, v, do = (device_tensor(d[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return q, k, v, do, o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 7, 33, 64, 65, 127, 129, 200, 1000])
+def test_bwd_sweep_vs_oracle(fa, T, causal, D):
+    print(f"case bwd T={T} D={D} causal={causal}", flush=True)
+    d = synth.make_inputs(1, 2, T, D, "bf16", seed=T * 3 + D, with_do=True)
+    scale = 1.0 / math.sqrt(D)
+    *_, dq, dk, dv = _gpu_fwd_bwd(fa, d, causal, scale)
+    q64, k64, v64, do64 = (as_f64(d[n], "bf16") for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, scale, causal)
+    ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
+    for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+        _check_grad(host_f64(g), r, n)
+
+
+def test_bwd_batch_heads(fa):
+    for causal in (False, True):
+        d = synth.make_inputs(2, 3, 150, 64, "bf16", seed=21, with_do=True)
+        *_, dq, dk, dv = _gpu_fwd_bwd(fa, d, causal, 0.125)
+        q64, k64, v64, do64 = (as_f64(d[n], "bf16") for n in ("q", "k", "v", "do"))
+        o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, 0.125, causal)
+        ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, 0.125, causal)
+        for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+            _check_grad(host_f64(g), r, n)
+
+
+def test_workload_backward_causal_t4096(fa):
+    w = synth.WORKLOADS["bwd_bf16_b2h16t4096d128_causal"]
+    d = synth.make_workload_inputs(w)
+    q, k, v, do, o, lse, dq, dk, dv = _gpu_fwd_bwd(fa, d, w.causal, w.scale)
+    # oracle-free properties over every head: each row of P sums to 1, so the
+    # key-sum of dV equals the query-sum of dO; each row of dS sums to 0, so the
+    # key-sum of dK vanishes.
+    sum_dv = dv.float().sum(dim=2)
+    sum_do = do.float().sum(dim=2)
+    assert (sum_dv - sum_do).abs().max().item() < 0.5
+    assert dk.float().sum(dim=2).abs().max().item() < 0.5
+    report = []
+    for idx in (0, 17, 31):
+        b, h = divmod(idx, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        q64, k64, v64, do64 = (as_f64(d[n][sl], "bf16") for n in ("q", "k", "v", "do"))
+        o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, w.scale, True)
+        ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, w.scale, True)
+        for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+            report.append((idx, n) + _check_grad(host_f64(g[sl]), r, f"head {idx} {n}"))
+    print("B=2 H=16 T=4096 D=128 causal backward (head, grad, max-abs, entries>=8):", report)
+
+
+def test_bwd_deterministic(fa):
+    d = synth.make_inputs(1, 4, 700, 128, "bf16", seed=22, with_do=True)
+    r1 = _gpu_fwd_bwd(fa, d, True, 0.09)
+    q, k, v, do, o, lse = r1[:6]
+    r2 = fa.fa_bwd(q, k, v, o, do, lse, causal=True, scale=0.09)
+    torch.cuda.synchronize()
+    for a, b in zip(r1[6:], r2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_zero_upstream_gradient(fa):
+    d = synth.make_inputs(1, 2, 300, 64, "bf16", seed=23)
+    q, k, v = (device_tensor(d[n], "bf16") for n in "qkv")
+    o, lse = fa.fa_fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, torch.zeros_like(o), lse, causal=True)
+    for g in (dq, dk, dv):
+        assert g.abs().max().item() == 0.0
+
+
+def test_bwd_argument_errors(fa):
+    import ctypes
+    lib = fa.load_library()
+    x = torch.zeros(1, 1, 64, 64, device="cuda", dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 64, device="cuda")
+    g = torch.full_like(x, 3.0)
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    p = x.data_ptr()
+
+    def call(ws_bytes=256, dtype=1, D=64):
+        return lib.fa_bwd(p, p, p, p, p, lse.data_ptr(), g.data_ptr(), g.data_ptr(), g.data_ptr(),
+                          ws.data_ptr(), ws_bytes, 1, 1, 64, D, ctypes.c_float(0.1), 1, dtype, None)
+
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 64) == 256
+    assert call(ws_bytes=255) == fa._lib.FA_ERR_ARG
+    assert call(dtype=0) == fa._lib.FA_ERR_DTYPE
+    assert call(D=96) == fa._lib.FA_ERR_HEADDIM
+    torch.cuda.synchronize()
+    assert bool((g == 3.0).all())
