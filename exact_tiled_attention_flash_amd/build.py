@@ -22,7 +22,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 ARCH = "gfx950"
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-fno-honor-nans", "-mno-amdgpu-ieee"]
+# per-source extra device flags
+EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", "-Wall",
           "-Wno-unused-function"]
 
@@ -43,10 +46,14 @@ def _compile(src: str, asm_dir: str | None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [_hipcc(), f"--offload-arch={ARCH}", *COMMON, "-c", src, "-o", obj]
     if src.endswith(".hip"):
-        cmd += DEVICE_FLAGS
+        cmd += DEVICE_FLAGS + EXTRA.get(os.path.basename(src), [])
         if asm_dir:
-            cmd += ["--save-temps"]
-    res = subprocess.run(cmd, cwd=asm_dir or BUILD, capture_output=True, text=True)
+            asm = os.path.join(asm_dir, os.path.basename(src) + ".s")
+            subprocess.run([_hipcc(), f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
+                            *EXTRA.get(os.path.basename(src), []),
+                            "--cuda-device-only", "-S", src, "-o", asm],
+                           capture_output=True, text=True, check=True)
+    res = subprocess.run(cmd, cwd=BUILD, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "is not a recognized feature for this target" not in l)
     if res.returncode != 0:
@@ -74,6 +81,6 @@ def build(asm_dir: str | None = None, jobs: int = 8) -> str:
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
-    ap.add_argument("--asm", default=None, help="keep device assembly (--save-temps) in this dir")
+    ap.add_argument("--asm", default=None, help="also write device assembly (.s) of each HIP source to this dir")
     args = ap.parse_args()
     print(build(args.asm))

@@ -7,24 +7,41 @@
 // diagonal tiles are masked element-wise) and section 5 (one program per
 // (query tile, batch*head)). "Triton FlashAttention-2 forward", "The kernel"
 // (queries outermost, P rounded to the input dtype before the P V product,
-// row sums in fp32, masked loads read zeros beyond T).
+// row sums in fp32, masked loads read zeros beyond T). Section 2 of the lab
+// page notes that subtracting any constant from the exponents and
+// multiplying back is exact; this kernel uses that freedom (see "lazy
+// rescale" below).
 //
 // gfx950 mapping
-//   * Workgroup: 256 threads = 4 waves; 128 queries (32 per wave) of one
-//     (b, h). Key tiles of 64 are streamed through LDS, double-buffered: the
-//     global loads of tile j+1 are in flight while tile j is computed.
-//   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so that
-//     lane l owns query (l % 32): a row's 64 scores sit in 32 registers of
-//     lane l and 32 of lane l^32, so the row max needs one cross-lane swap
-//     and the row sum none until the end.
-//   * The S^T accumulator layout is exactly the B-operand layout of
-//     O^T += V^T P^T over 16-key chunks, so P never leaves registers; V is
-//     stored transposed in LDS so the A operand is two 8-byte reads.
-//   * exp(x) is evaluated as exp2(x * scale * log2 e) with one FMA.
+//   * Workgroup: 256 threads = 4 waves, one per SIMD; 256 queries of one
+//     (b, h), 64 per wave as two 32-query blocks. Every K / V operand read
+//     from LDS feeds two matrix-core products (one per query block), which
+//     halves LDS traffic per flop compared with 32 queries per wave; LDS
+//     bandwidth (128 B/clk/CU) is the limiter otherwise.
+//   * Key tiles of 64 are double-buffered in LDS; the global loads of tile
+//     j+1 are in flight while tile j is computed. K and V are stored
+//     row-major with padded pitches chosen for conflict-free reads.
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane: a
+//     row's 64 scores sit in 32 registers of lane l and 32 of lane l^32.
+//     The S^T accumulator layout is the B-operand layout of O^T += V^T P^T,
+//     so P never leaves registers. The V^T A operand comes straight from the
+//     row-major V tile through the transposing LDS read (ds_read_b64_tr_b16):
+//     within each 16-lane group, lane i addresses V[key0 + i/4][d0 + 4(i%4)]
+//     and lane j receives V[key0 .. key0+3][d0 + j].
+//   * exp(x) is exp2(x * scale * log2 e): one FMA and one v_exp_f32.
+//   * Lazy rescale: a row's reference max is only moved (and acc, l
+//     rescaled) when the new tile max exceeds it by more than 2^8 in the
+//     exponent; otherwise P <= 2^8 is accumulated against the stale
+//     reference. acc / l is unchanged by the choice of reference, and the
+//     bound keeps every fp32 value far from overflow. The branch is taken
+//     on the first tile and rarely afterwards.
+//   * The loop over key tiles is split: tiles that need no mask run in a
+//     lean main loop; the causal diagonal tiles and the ragged last tile
+//     run in a masked tail, where fully hidden 32-query blocks are skipped.
 //   * Causal grid order is heaviest query tile first; consecutive workgroup
-//     ids walk the (b, h) index fastest, which keeps all tiles of one head on
-//     one XCD (workgroups are dealt to the 8 XCDs round-robin) so K and V of
-//     a head are shared through that XCD's L2.
+//     ids walk (b, h) fastest, which keeps all tiles of one head on one XCD
+//     (workgroups are dealt to the 8 XCDs round-robin) so K and V of a head
+//     are shared through that XCD's L2.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -33,89 +50,82 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBlockM = 128;
-constexpr int kBlockN = 64;
+constexpr int kBlockM = 256;   // queries per workgroup
+constexpr int kBlockN = 64;    // keys per tile
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct FwdTile {
-  static constexpr int kPitch = D + 8;          // LDS row pitch of K (bf16 elements)
-  static constexpr int vPitch = kBlockN + 4;    // LDS row pitch of V^T
-  static constexpr int kElems = kBlockN * kPitch;
-  static constexpr int vElems = D * vPitch;
-  static constexpr int stageElems = kElems + vElems;
-  static constexpr int chunks = D / 8;                          // 16-byte chunks per row
-  static constexpr int kLoads = kBlockN * chunks / kThreads;    // K chunks per thread
-  static constexpr int vKeys = kBlockN * chunks / kThreads;     // keys per V unit
-  static_assert(kLoads * kThreads == kBlockN * chunks, "K tile split");
-  static_assert(vKeys == 2 || vKeys == 4, "V unit");
+  static constexpr int CH = D / 8;                      // 16-byte chunks per row
+  static constexpr int RB = D * 2;                      // bytes per row (unpadded)
+  static constexpr int tileBytes = kBlockN * RB;        // one K or V tile
+  static constexpr int stageBytes = 2 * tileBytes;      // K tile, then V tile
+  static constexpr int loadsPerWave = kBlockN * CH / kThreads;  // 16-byte loads per lane per tensor
+  static_assert(loadsPerWave * kThreads == kBlockN * CH, "tile split");
+  // XOR swizzle of the 16-byte chunks of a row, so that 16 lanes reading one
+  // logical chunk of 16 consecutive rows hit 16 different bank groups.
+  __device__ static __forceinline__ int swz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  }
+  __device__ static __forceinline__ int offset(int row, int lchunk) {
+    return row * RB + ((lchunk ^ swz(row)) << 4);
+  }
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue the direct global->LDS loads of key tile k0 (K and V) into `stage`.
+// Lane `lane` of load i of wave `wave` fills LDS bytes [16 u, 16 u + 16) of
+// the tile, u = (wave * loadsPerWave + i) * 64 + lane, i.e. physical chunk
+// u % CH of row u / CH; it fetches the logical chunk that the swizzle maps
+// there. Rows at or beyond T are clamped to row T - 1: such keys are masked
+// out of S and their V rows only ever meet P = 0.
 template <int D>
-__device__ __forceinline__ void load_kv(const uint16_t* __restrict__ Kh,
-                                        const uint16_t* __restrict__ Vh, int k0, int T,
-                                        int tid, u32x4 (&kr)[FwdTile<D>::kLoads],
-                                        u32x4 (&vr)[FwdTile<D>::vKeys]) {
+__device__ __forceinline__ void issue_kv(uint8_t* stage, const uint16_t* __restrict__ Kh,
+                                         const uint16_t* __restrict__ Vh, int k0, int T,
+                                         int wave, int lane) {
   using Tl = FwdTile<D>;
 #pragma unroll
-  for (int i = 0; i < Tl::kLoads; ++i) {
-    const int u = tid + i * kThreads;
-    const int key = k0 + u / Tl::chunks;
-    const int ch = u % Tl::chunks;
-    kr[i] = key < T ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + ch * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int ch = tid % Tl::chunks;
-  const int g = tid / Tl::chunks;
-#pragma unroll
-  for (int i = 0; i < Tl::vKeys; ++i) {
-    const int key = k0 + g * Tl::vKeys + i;
-    vr[i] = key < T ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + ch * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < Tl::loadsPerWave; ++i) {
+    const int slot = wave * Tl::loadsPerWave + i;
+    const int u = slot * 64 + lane;
+    const int row = u / Tl::CH;
+    const int lc = (u % Tl::CH) ^ Tl::swz(row);
+    const size_t g = (size_t)min(k0 + row, T - 1) * D + lc * 8;
+    __builtin_amdgcn_global_load_lds(Kh + g, (lds_void*)(stage + slot * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(Vh + g, (lds_void*)(stage + Tl::tileBytes + slot * 1024), 16,
+                                     0, 0);
   }
 }
 
-// bf16 element e (0..7) of a 16-byte chunk, moved to the low half of a dword.
-__device__ __forceinline__ uint32_t elem_lo(const u32x4& x, int e) {
-  const uint32_t w = x[e >> 1];
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
+// A operand of O^T += V^T P^T for d rows [32 db, 32 db + 32) and keys 16 cc + {4h..4h+3,
+// 8+4h..8+4h+3}: two transposing reads from the row-major (swizzled) V tile.
 template <int D>
-__device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, int tid,
-                                         const u32x4 (&kr)[FwdTile<D>::kLoads],
-                                         const u32x4 (&vr)[FwdTile<D>::vKeys]) {
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* Vs, int db, int cc, int lane) {
   using Tl = FwdTile<D>;
-  uint16_t* Ks = stage;
-  uint16_t* Vt = stage + Tl::kElems;
-#pragma unroll
-  for (int i = 0; i < Tl::kLoads; ++i) {
-    const int u = tid + i * kThreads;
-    *reinterpret_cast<u32x4*>(Ks + (u / Tl::chunks) * Tl::kPitch + (u % Tl::chunks) * 8) = kr[i];
-  }
-  const int ch = tid % Tl::chunks;
-  const int g = tid / Tl::chunks;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint16_t* dst = Vt + (ch * 8 + e) * Tl::vPitch + g * Tl::vKeys;
-    if constexpr (Tl::vKeys == 4) {
-      u32x2 w = {elem_lo(vr[0], e) | (elem_lo(vr[1], e) << 16),
-                 elem_lo(vr[2], e) | (elem_lo(vr[3], e) << 16)};
-      *reinterpret_cast<u32x2*>(dst) = w;
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) = elem_lo(vr[0], e) | (elem_lo(vr[1], e) << 16);
-    }
-  }
+  const int g = lane >> 4, i = lane & 15;
+  const int key = 16 * cc + 4 * (g >> 1) + (i >> 2);
+  const int d0 = db * 32 + (g & 1) * 16 + 4 * (i & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(Vs + Tl::offset(key, d0 >> 3) + (d0 & 7) * 2));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(Vs + Tl::offset(key + 8, d0 >> 3) + (d0 & 7) * 2));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int T, int BH, int nq, float c) {
   using Tl = FwdTile<D>;
   constexpr int nD = D / 32;   // 32-row blocks of O^T
   constexpr int nK = D / 16;   // k-steps of S^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Tl::stageElems];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Tl::stageBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -128,145 +138,164 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   int qt = L / BH;
   if (CAUSAL) qt = nq - 1 - qt;
   const int q0 = qt * kBlockM;
-  const int qw0 = q0 + wave * 32;
-  const int qrow = qw0 + l32;
+  const int qw0 = q0 + wave * 64;
 
   const size_t base = (size_t)bh * T * D;
   const uint16_t* Qh = Q + base;
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
 
-  // Q^T fragments stay in registers: lane holds query qrow, d = 16*kk + 8*h + 0..7.
-  bf16x8 qf[nK];
+  // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
+  // d = 16 kk + 8 h + 0..7.
+  bf16x8 qf[2][nK];
 #pragma unroll
-  for (int kk = 0; kk < nK; ++kk) {
-    u32x4 x = qrow < T ? *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + kk * 16 + h * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
-    qf[kk] = as_bf16x8(x);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw0 + 32 * qb + l32;
+#pragma unroll
+    for (int kk = 0; kk < nK; ++kk) {
+      u32x4 x = qrow < T ? *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + kk * 16 + h * 8)
+                         : u32x4{0u, 0u, 0u, 0u};
+      qf[qb][kk] = as_bf16x8(x);
+    }
   }
 
   const int kend = CAUSAL ? min(T, q0 + kBlockM) : T;
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  // tiles [0, nfull) need no mask for any query of this workgroup
+  int nfull = (CAUSAL ? min(q0, T) : T) / kBlockN;
+  nfull = min(nfull, ntiles);
 
-  f32x16 acc[nD];
+  f32x16 acc[2][nD];
 #pragma unroll
-  for (int db = 0; db < nD; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;
-  float l_run = 0.f;
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < nD; ++db) acc[qb][db] = f32x16{};
+  float m_ref[2] = {kNegInf, kNegInf};   // running row max (raw score units)
+  float l_run[2] = {0.f, 0.f};           // partial row sums over this lane's key half
 
-  u32x4 kr[Tl::kLoads];
-  u32x4 vr[Tl::vKeys];
-  load_kv<D>(Kh, Vh, 0, T, tid, kr, vr);
-  store_kv<D>(smem, tid, kr, vr);
+  issue_kv<D>(smem, Kh, Vh, 0, T, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * kBlockN;
-    const bool more = j + 1 < ntiles;
-    if (more) load_kv<D>(Kh, Vh, k0 + kBlockN, T, tid, kr, vr);
-
-    const uint16_t* Ks = smem + (j & 1) * Tl::stageElems;
-    const uint16_t* Vt = Ks + Tl::kElems;
-    const bool wave_skip = CAUSAL && (k0 > qw0 + 31);
-    if (!wave_skip) {
-      // S^T for keys k0 + [0, 32) and k0 + [32, 64)
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // Scores -> probabilities for one 32-query block; returns P^T as 4 bf16 B operands.
+  auto softmax_block = [&](f32x16 (&s)[2], int qb, bool masked, int k0, bf16x8 (&p)[4]) {
+    const int qrow = qw0 + 32 * qb + l32;
+    uint32_t valid = 0xffffffffu;
+    if (masked) {
+      valid = 0u;
 #pragma unroll
-      for (int kk = 0; kk < nK; ++kk) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(Ks + l32 * Tl::kPitch + kk * 16 + h * 8);
-        const u32x4 a1 =
-            *reinterpret_cast<const u32x4*>(Ks + (32 + l32) * Tl::kPitch + kk * 16 + h * 8);
-        s0 = mfma32(as_bf16x8(a0), qf[kk], s0);
-        s1 = mfma32(as_bf16x8(a1), qf[kk], s1);
-      }
-
-      const bool need_mask = (k0 + kBlockN > T) || (CAUSAL && (k0 + kBlockN - 1 > qw0));
-      uint32_t valid = 0xffffffffu;  // bit r: key of s0[r]; bit 16+r: key of s1[r]
-      if (need_mask) {
-        valid = 0u;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool v0 = key < T && (!CAUSAL || key <= qrow);
-          const bool v1 = key + 32 < T && (!CAUSAL || key + 32 <= qrow);
-          valid |= (v0 ? 1u : 0u) << r;
-          valid |= (v1 ? 1u : 0u) << (16 + r);
-          s0[r] = v0 ? s0[r] : kNegInf;
-          s1[r] = v1 ? s1[r] : kNegInf;
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool ok = key < T && (!CAUSAL || key <= qrow);
+          valid |= (ok ? 1u : 0u) << (16 * kb + r);
+          s[kb][r] = ok ? s[kb][r] : kNegInf;
         }
-      }
-
-      float mx = kNegInf;
+    }
+    float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast((m_run - m_use) * c);
-      const float mc = m_use * c;
-
-      float psum = 0.f;
+    for (int r = 0; r < 16; r += 2)
+      mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_old = m_ref[qb];
+    const float m_new = fmaxf(m_old, mx);
+    // alpha = exp(m_old - m_new) (1 when the max did not move, 0 on the row's first tile)
+    const float alpha = (m_old == kNegInf) ? 0.f : exp2_fast((m_old - m_new) * c);
+    m_ref[qb] = m_new;
+    l_run[qb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < nD; ++db) acc[qb][db] *= alpha;
+    const float mc = (m_new == kNegInf ? 0.f : m_new) * c;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = exp2_fast(fmaf(s0[r], c, -mc));
-        s1[r] = exp2_fast(fmaf(s1[r], c, -mc));
+        float e = exp2_fast(fmaf(s[kb][r], c, -mc));
+        if (masked) e = (valid >> (16 * kb + r)) & 1u ? e : 0.f;
+        s[kb][r] = e;
       }
-      if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] = (valid >> r) & 1u ? s0[r] : 0.f;
-          s1[r] = (valid >> (16 + r)) & 1u ? s1[r] : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      ps0 += s[0][r];
+      ps1 += s[1][r];
+    }
+    l_run[qb] += ps0 + ps1;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const f32x16& sv = s[cc >> 1];
+      const int o = (cc & 1) * 8;
+      u32x4 w = {pack_bf16x2(sv[o + 0], sv[o + 1]), pack_bf16x2(sv[o + 2], sv[o + 3]),
+                 pack_bf16x2(sv[o + 4], sv[o + 5]), pack_bf16x2(sv[o + 6], sv[o + 7])};
+      p[cc] = as_bf16x8(w);
+    }
+  };
+
+  auto tile = [&](int j, bool masked) {
+    const int k0 = j * kBlockN;
+    const bool more = j + 1 < ntiles;
+    if (more) issue_kv<D>(smem + ((j + 1) & 1) * Tl::stageBytes, Kh, Vh, k0 + kBlockN, T, wave, lane);
+    const uint8_t* Ks = smem + (j & 1) * Tl::stageBytes;
+    const uint8_t* Vs = Ks + Tl::tileBytes;
+    // which 32-query blocks of this wave see any key of the tile
+    const bool act0 = !masked || !CAUSAL || k0 <= qw0 + 31;
+    const bool act1 = !masked || !CAUSAL || k0 <= qw0 + 63;
+    if (act1) {
+      f32x16 s0[2] = {f32x16{}, f32x16{}}, s1[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < nK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = as_bf16x8(
+              *reinterpret_cast<const u32x4*>(Ks + Tl::offset(kb * 32 + l32, 2 * kk + h)));
+          if (act0) s0[kb] = mfma32(a, qf[0][kk], s0[kb]);
+          s1[kb] = mfma32(a, qf[1][kk], s1[kb]);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) psum += s0[r] + s1[r];
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < nD; ++db) acc[db] *= alpha;
-
-      // P^T in bf16: chunk cc covers keys k0 + 16*cc + {4h..4h+3, 8+4h..8+4h+3}
-      bf16x8 p[4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const f32x16& s = (cc < 2) ? s0 : s1;
-        const int o = (cc & 1) * 8;
-        u32x4 w = {pack_bf16x2(s[o + 0], s[o + 1]), pack_bf16x2(s[o + 2], s[o + 3]),
-                   pack_bf16x2(s[o + 4], s[o + 5]), pack_bf16x2(s[o + 6], s[o + 7])};
-        p[cc] = as_bf16x8(w);
-      }
+      bf16x8 p0[4], p1[4];
+      const bool mask0 = masked && (k0 + kBlockN > T || (CAUSAL && k0 + kBlockN - 1 > qw0));
+      const bool mask1 = masked && (k0 + kBlockN > T || (CAUSAL && k0 + kBlockN - 1 > qw0 + 32));
+      if (act0) softmax_block(s0, 0, mask0, k0, p0);
+      softmax_block(s1, 1, mask1, k0, p1);
 #pragma unroll
       for (int db = 0; db < nD; ++db) {
-        const uint16_t* vrow = Vt + (db * 32 + l32) * Tl::vPitch + 4 * h;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * cc);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * cc + 8);
-          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = mfma32(as_bf16x8(a), p[cc], acc[db]);
+          const bf16x8 a = v_operand<D>(Vs, db, cc, lane);
+          if (act0) acc[0][db] = mfma32(a, p0[cc], acc[0][db]);
+          acc[1][db] = mfma32(a, p1[cc], acc[1][db]);
         }
       }
     }
-
-    if (more) store_kv<D>(smem + ((j + 1) & 1) * Tl::stageElems, tid, kr, vr);
+    // the next tile's loads (this wave's) have landed; the barrier makes every
+    // wave's part visible and frees this stage for the loads of tile j + 2
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
 
-  const float l_tot = l_run + swap_halves(l_run);
-  if (qrow < T) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = O + base + (size_t)qrow * D;
+  for (int j = 0; j < nfull; ++j) tile(j, false);
+  for (int j = nfull; j < ntiles; ++j) tile(j, true);
+
 #pragma unroll
-    for (int db = 0; db < nD; ++db) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = qw0 + 32 * qb + l32;
+    const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+    if (qrow < T) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = O + base + (size_t)qrow * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = db * 32 + 8 * g + 4 * h;
-        u32x2 w = {pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
-                   pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      for (int db = 0; db < nD; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * h;
+          u32x2 w = {pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv),
+                     pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = w;
+        }
       }
+      if (h == 0) LSE[(size_t)bh * T + qrow] = (m_ref[qb] * c + log2_fast(l_tot)) * kLn2;
     }
-    if (h == 0) LSE[(size_t)bh * T + qrow] = (m_run * c + log2_fast(l_tot)) * kLn2;
   }
 }
 
