@@ -54,6 +54,26 @@ def _time_launches(torch, fn, steps, warmup):
     return total, per, wall_ms
 
 
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_b4h16t4096d128_causal_traffic.json")
+FWD_SOURCE = os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc", "fa_fwd_bf16.hip")
+
+
+def committed_traffic(flops):
+    """HBM bytes per launch of the forward kernel from the committed rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (scaled by the same counters on a copy of known size), provided the kernel
+    source is unchanged since they were taken; else None."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    digest = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return {"bytes_per_launch": rec["hbm_bytes_per_launch"], "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+
+
 def cpu_baseline(w, d, budget_s: float):
     """Time the float64 oracle on whole (b, h) heads of the same inputs, in order,
     until budget_s has passed."""
@@ -89,6 +109,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device-to-device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path; "
@@ -144,6 +166,19 @@ def main():
                      "algorithmic_bytes_per_launch": metrics.fwd_bytes(w.B, w.H, w.T, w.D, 2)},
         "wall_ms_timed_region": round(wall_ms, 3),
     }
+
+    traffic = committed_traffic(flops)
+    if traffic is not None:
+        out["roofline"]["traffic"] = traffic["bytes_per_launch"]
+        out["roofline"]["traffic_source"] = traffic["source"]
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = COPY_BYTES
 
     lib = fa.load_library()
     if not args.no_backward and hasattr(lib, "fa_bwd"):
