@@ -37,7 +37,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m exact_tiled_attention_flash_amd.build`")
+                          "`python exact_tiled_attention_flash_amd/build.py`")
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_abi_version.restype = i

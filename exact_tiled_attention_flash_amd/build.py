@@ -1,6 +1,7 @@
 """Build libfa.so (the HIP kernels for gfx950 plus the C ABI) in-tree with hipcc.
 
-Usage: python -m exact_tiled_attention_flash_amd.build [--asm DIR]
+Usage: python exact_tiled_attention_flash_amd/build.py [--asm DIR]
+(run by path: importing the package itself needs the built library)
 
 Each source compiles in its own hipcc process (in parallel), then one link
 step writes exact_tiled_attention_flash_amd/libfa.so. Packed fp32 vector

@@ -71,7 +71,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_workspace_bytes(int B, int H, int T, int D) {
   if (check_sizes(B, H, T, D) != FA_OK) return 0;
-  return sizeof(float) * size_t(B) * size_t(H) * size_t(T);
+  return 2 * sizeof(float) * size_t(B) * size_t(H) * size_t(T);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -1,50 +1,49 @@
 // Attention backward, bf16 storage, fp32 accumulation: three hand-written gfx950 kernels.
 //
-// Method: "Lab 06 - Attention kernels", section 4: with P = exp(S - LSE)
-// recomputed per tile from the saved LSE, dV = P^T dO, dP = dO V^T,
-// dS = P * (dP - D) where D_i = rowsum(dO * O)_i (an O(T d) pass instead of
-// a reduction over P), dQ = dS K scale and dK = dS^T Q scale; the causal
-// mask is applied before the exponential exactly as in the forward ("Common
-// bugs"). Work split per the page's "Stretch" list: one kernel with key
-// tiles outer (dK, dV accumulate in registers) and one with query tiles
-// outer (dQ accumulates in registers), so no atomics are needed and the
-// result is deterministic.
+// Method: "Lab 06 - Attention kernels", section 4: with P = exp(S - LSE) recomputed per tile
+// from the saved LSE, dV = P^T dO, dP = dO V^T, dS = P * (dP - D) where D_i = rowsum(dO * O)_i
+// (an O(T d) pass instead of a reduction over P), dQ = dS K scale and dK = dS^T Q scale; the
+// causal mask is applied before the exponential exactly as in the forward ("Common bugs").
+// Work split per the page's "Stretch" list: one kernel with key tiles outer (dK, dV
+// accumulate in registers) and one with query tiles outer (dQ accumulates in registers), so
+// no atomics are needed and the result is deterministic.
 //
-//   bwd_pre_kernel   D_i = sum_d dO_id O_id                      (HBM-bound)
-//   bwd_dkdv_kernel  workgroup = 128 keys (32 per wave) of one (b, h); loops
-//                    over 64-query tiles from the diagonal down. Per wave:
-//                    S = Q K^T and dP = dO V^T with K, V held in registers
-//                    (lane = key), then dV^T += dO^T P and dK^T += Q^T dS,
-//                    whose A operands come from transposed Q / dO tiles in LDS.
-//   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key
-//                    tiles up to the diagonal. Per wave: S^T = K Q^T and
-//                    dP^T = V dO^T with Q, dO in registers (lane = query),
-//                    then dQ^T += K^T dS^T from a transposed K tile in LDS.
-// The accumulator layout of S / S^T doubles as the B-operand layout of the
-// following product (k-slots permuted the same way for both operands), so P
-// and dS never leave registers.
+//   bwd_pre_kernel   D_i = sum_d dO_id O_id and LSE_i * log2(e), into the workspace (HBM-bound)
+//   bwd_dkdv_kernel  workgroup = 128 keys (32 per wave) of one (b, h); loops over 64-query
+//                    tiles from the diagonal down. Per wave: S = Q K^T and dP = dO V^T with
+//                    K, V held in registers (lane = key), then dV^T += dO^T P and
+//                    dK^T += Q^T dS, whose A operands are transposing LDS reads of the
+//                    row-major Q and dO tiles.
+//   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key tiles up to
+//                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
+//                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
+//                    read of the row-major K tile.
+// Tiles reach LDS by direct HBM -> LDS loads (no staging registers), double-buffered; the
+// accumulator layout of S / S^T doubles as the B-operand layout of the following product
+// (k-slots permuted the same way for both operands), so P and dS never leave registers.
 
 #include "fa_common.h"
 #include "fa_launch.h"
-#include "fa_tile.h"
+#include "fa_swz.h"
 
 namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kPosInf = __builtin_inff();
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-// ------------------------------------------------------------------ D_i = rowsum(dO * O)
+// ------------------------------------------------------------------ D_i, LSE_i * log2(e)
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                            const uint16_t* __restrict__ dO,
-                                                           float* __restrict__ Dv, int64_t rows) {
+                                                           const float* __restrict__ LSE,
+                                                           float* __restrict__ Dv,
+                                                           float* __restrict__ L2, int64_t rows) {
   constexpr int LPR = D / 8;             // lanes per row, one 16-byte chunk each
   constexpr int RPB = kThreads / LPR;    // rows per workgroup
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -58,7 +57,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (ch == 0 && row < rows) Dv[row] = s;
+  if (ch == 0 && row < rows) {
+    Dv[row] = s;
+    L2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // Store a 32 x D block held as D/32 accumulators (lane = row, registers = d).
@@ -76,33 +78,35 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* __restrict__ dst, cons
   }
 }
 
+// 64 fp32 values of rows [row0, row0 + 64) (clamped to T - 1) straight into LDS; one wave.
+__device__ __forceinline__ void issue_stats(uint8_t* dst, const float* __restrict__ src, int row0,
+                                            int T, int lane) {
+  __builtin_amdgcn_global_load_lds(src + min(row0 + lane, T - 1), (lds_void*)dst, 4, 0, 0);
+}
+
 // ------------------------------------------------------------------ dK, dV
 constexpr int kKeysPerWG = 128;
 constexpr int kQTile = 64;
 
 template <int D>
-struct DkdvSmem {
-  static constexpr int rPitch = D + 8;        // row-major copies (bf16 elements)
-  static constexpr int cPitch = kQTile + 4;   // transposed copies
-  static constexpr int qRows = 0;
-  static constexpr int qCols = qRows + kQTile * rPitch;
-  static constexpr int doRows = qCols + D * cPitch;
-  static constexpr int doCols = doRows + kQTile * rPitch;
-  static constexpr int bf16Elems = doCols + D * cPitch;
-  static constexpr int stageBytes = bf16Elems * 2 + 2 * kQTile * 4;  // + lse2[64], dvec[64]
-  static_assert(stageBytes % 16 == 0, "stage alignment");
+struct DkdvStage {
+  static constexpr int q = 0;
+  static constexpr int dO = SwzTile<D>::bytes;
+  static constexpr int lse2 = 2 * SwzTile<D>::bytes;
+  static constexpr int dvec = lse2 + 4 * kQTile;
+  static constexpr int bytes = dvec + 4 * kQTile;
+  static_assert(bytes % 256 == 0, "stage alignment (one full pass over the LDS banks)");
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, float c, float scale) {
-  using Sm = DkdvSmem<D>;
-  using Tile = RowTile<D>;
+  using St = DkdvStage<D>;
   constexpr int nD = D / 32;
   constexpr int nK = D / 16;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Sm::stageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * St::bytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -116,6 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
   const size_t base = (size_t)bh * T * D;
+  const size_t rbase = (size_t)bh * T;
 
   bf16x8 kf[nK], vf[nK];
 #pragma unroll
@@ -135,39 +140,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int nqt = (T + kQTile - 1) / kQTile;
   const int qt0 = CAUSAL ? k0 / kQTile : 0;
 
-  u32x4 qr[Tile::RPT], dor[Tile::RPT];
-  float stat = 0.f;  // thread t < 64: lse2 of query t; 64 <= t < 128: D of query t - 64
-  auto fetch = [&](int qt) {
+  auto fetch = [&](int qt, uint8_t* st) {
     const int q0 = qt * kQTile;
-    Tile::load(Q + base, q0, T, tid, qr);
-    Tile::load(dO + base, q0, T, tid, dor);
-    if (tid < 2 * kQTile) {
-      const int q = q0 + (tid & (kQTile - 1));
-      if (tid < kQTile) stat = q < T ? LSE[(size_t)bh * T + q] * kLog2e : kPosInf;
-      else stat = q < T ? Dv[(size_t)bh * T + q] : 0.f;
-    }
-  };
-  auto stash = [&](uint8_t* st) {
-    uint16_t* b = reinterpret_cast<uint16_t*>(st);
-    Tile::store_rows(b + Sm::qRows, Sm::rPitch, tid, qr);
-    Tile::store_cols(b + Sm::qCols, Sm::cPitch, tid, qr);
-    Tile::store_rows(b + Sm::doRows, Sm::rPitch, tid, dor);
-    Tile::store_cols(b + Sm::doCols, Sm::cPitch, tid, dor);
-    if (tid < 2 * kQTile) reinterpret_cast<float*>(st + Sm::bf16Elems * 2)[tid] = stat;
+    issue_tile<D>(st + St::q, Q + base, q0, T, wave, lane);
+    issue_tile<D>(st + St::dO, dO + base, q0, T, wave, lane);
+    if (wave == 0) issue_stats(st + St::lse2, L2 + rbase, q0, T, lane);
+    if (wave == 1) issue_stats(st + St::dvec, Dv + rbase, q0, T, lane);
   };
 
-  fetch(qt0);
-  stash(smem);
+  fetch(qt0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int qt = qt0; qt < nqt; ++qt) {
     const int it = qt - qt0;
-    const bool more = qt + 1 < nqt;
-    if (more) fetch(qt + 1);
-    const uint8_t* st = smem + (it & 1) * Sm::stageBytes;
-    const uint16_t* sb = reinterpret_cast<const uint16_t*>(st);
-    const float* lse2 = reinterpret_cast<const float*>(st + Sm::bf16Elems * 2);
-    const float* dvec = lse2 + kQTile;
+    if (qt + 1 < nqt) fetch(qt + 1, smem + ((it + 1) & 1) * St::bytes);
+    const uint8_t* st = smem + (it & 1) * St::bytes;
+    const uint8_t* Qs = st + St::q;
+    const uint8_t* dOs = st + St::dO;
+    const float* lse2 = reinterpret_cast<const float*>(st + St::lse2);
+    const float* dvec = reinterpret_cast<const float*>(st + St::dvec);
     const int q0 = qt * kQTile;
 
 #pragma unroll
@@ -177,12 +169,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < nK; ++kk) {
-        const int off = (qb * 32 + l32) * Sm::rPitch + kk * 16 + h * 8;
-        s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(sb + Sm::qRows + off)), kf[kk], s);
-        dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(sb + Sm::doRows + off)), vf[kk], dp);
+        s = mfma32(row_operand<D>(Qs, qb * 32 + l32, 2 * kk + h), kf[kk], s);
+        dp = mfma32(row_operand<D>(dOs, qb * 32 + l32, 2 * kk + h), vf[kk], dp);
       }
       // lane = key; register r = query qb0 + 8*(r/4) + 4h + (r%4)
-      const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (kw0 + 32 > T);
+      const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > T);
       f32x16 p, ds;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -194,33 +185,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           float pv = exp2_fast(fmaf(s[r], c, -l4[i]));
           if (need_mask) {
             const int qi = qb0 + 8 * g + 4 * h + i;
-            const bool ok = key < T && (!CAUSAL || key <= qi);
+            const bool ok = qi < T && (!CAUSAL || key <= qi);
             pv = ok ? pv : 0.f;
           }
           p[r] = pv;
           ds[r] = pv * (dp[r] - d4[i]);
         }
       }
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int o = cc * 8;
-        pb[cc] = as_bf16x8(u32x4{pack_bf16x2(p[o], p[o + 1]), pack_bf16x2(p[o + 2], p[o + 3]),
-                                 pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7])});
-        dsb[cc] = as_bf16x8(u32x4{pack_bf16x2(ds[o], ds[o + 1]), pack_bf16x2(ds[o + 2], ds[o + 3]),
-                                  pack_bf16x2(ds[o + 4], ds[o + 5]), pack_bf16x2(ds[o + 6], ds[o + 7])});
-      }
+      const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 8)};
+      const bf16x8 dsb[2] = {pack8(ds, 0), pack8(ds, 8)};
 #pragma unroll
       for (int db = 0; db < nD; ++db) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const int crow = db * 32 + l32;
-          dv[db] = mfma32(load_perm_k(sb + Sm::doCols, Sm::cPitch, crow, qb * 32 + 16 * cc, h), pb[cc], dv[db]);
-          dk[db] = mfma32(load_perm_k(sb + Sm::qCols, Sm::cPitch, crow, qb * 32 + 16 * cc, h), dsb[cc], dk[db]);
+          dv[db] = mfma32(tr_operand<D>(dOs, db, qb * 32 + 16 * cc, lane), pb[cc], dv[db]);
+          dk[db] = mfma32(tr_operand<D>(Qs, db, qb * 32 + 16 * cc, lane), dsb[cc], dk[db]);
         }
       }
     }
-    if (more) stash(smem + ((it + 1) & 1) * Sm::stageBytes);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -234,27 +217,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 constexpr int kQueriesPerWG = 128;
 constexpr int kKTile = 64;
 
-template <int D>
-struct DqSmem {
-  static constexpr int rPitch = D + 8;
-  static constexpr int cPitch = kKTile + 4;
-  static constexpr int kRows = 0;
-  static constexpr int vRows = kRows + kKTile * rPitch;
-  static constexpr int kCols = vRows + kKTile * rPitch;
-  static constexpr int stageElems = kCols + D * cPitch;
-  static_assert((stageElems * 2) % 16 == 0, "stage alignment");
-};
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
     uint16_t* __restrict__ dQ, int T, int BH, int nq, float c, float scale) {
-  using Sm = DqSmem<D>;
-  using Tile = RowTile<D>;
+  using Tl = SwzTile<D>;
   constexpr int nD = D / 32;
   constexpr int nK = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Sm::stageElems];
+  constexpr int stageBytes = 2 * Tl::bytes;   // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * stageBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -278,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     qf[kk] = as_bf16x8(qrow < T ? *reinterpret_cast<const u32x4*>(Q + off) : u32x4{0u, 0u, 0u, 0u});
     dof[kk] = as_bf16x8(qrow < T ? *reinterpret_cast<const u32x4*>(dO + off) : u32x4{0u, 0u, 0u, 0u});
   }
-  const float lse2 = qrow < T ? LSE[(size_t)bh * T + qrow] * kLog2e : kPosInf;
+  const float lse2 = qrow < T ? L2[(size_t)bh * T + qrow] : 0.f;
   const float dval = qrow < T ? Dv[(size_t)bh * T + qrow] : 0.f;
 
   f32x16 dq[nD];
@@ -288,25 +260,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(T, q0 + kQueriesPerWG) : T;
   const int ntiles = (kend + kKTile - 1) / kKTile;
 
-  u32x4 kr[Tile::RPT], vr[Tile::RPT];
-  auto stash = [&](uint16_t* st) {
-    Tile::store_rows(st + Sm::kRows, Sm::rPitch, tid, kr);
-    Tile::store_cols(st + Sm::kCols, Sm::cPitch, tid, kr);
-    Tile::store_rows(st + Sm::vRows, Sm::rPitch, tid, vr);
+  auto fetch = [&](int j, uint8_t* st) {
+    issue_tile<D>(st, K + base, j * kKTile, T, wave, lane);
+    issue_tile<D>(st + Tl::bytes, V + base, j * kKTile, T, wave, lane);
   };
-  Tile::load(K + base, 0, T, tid, kr);
-  Tile::load(V + base, 0, T, tid, vr);
-  stash(smem);
+  fetch(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int k0 = j * kKTile;
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      Tile::load(K + base, k0 + kKTile, T, tid, kr);
-      Tile::load(V + base, k0 + kKTile, T, tid, vr);
-    }
-    const uint16_t* st = smem + (j & 1) * Sm::stageElems;
+    if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
+    const uint8_t* Ks = smem + (j & 1) * stageBytes;
+    const uint8_t* Vs = Ks + Tl::bytes;
     if (!(CAUSAL && k0 > qw0 + 31)) {
       f32x16 s[2], dp[2];
 #pragma unroll
@@ -315,9 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         dp[kb] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < nK; ++kk) {
-          const int off = (kb * 32 + l32) * Sm::rPitch + kk * 16 + h * 8;
-          s[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(st + Sm::kRows + off)), qf[kk], s[kb]);
-          dp[kb] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(st + Sm::vRows + off)), dof[kk], dp[kb]);
+          s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, 2 * kk + h), qf[kk], s[kb]);
+          dp[kb] = mfma32(row_operand<D>(Vs, kb * 32 + l32, 2 * kk + h), dof[kk], dp[kb]);
         }
       }
       // lane = query; register r of block kb = key k0 + 32 kb + 8*(r/4) + 4h + (r%4)
@@ -336,22 +301,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
           }
           ds[r] = pv * (dp[kb][r] - dval);
         }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int o = half * 8;
-          dsb[2 * kb + half] =
-              as_bf16x8(u32x4{pack_bf16x2(ds[o], ds[o + 1]), pack_bf16x2(ds[o + 2], ds[o + 3]),
-                              pack_bf16x2(ds[o + 4], ds[o + 5]), pack_bf16x2(ds[o + 6], ds[o + 7])});
-        }
+        dsb[2 * kb] = pack8(ds, 0);
+        dsb[2 * kb + 1] = pack8(ds, 8);
       }
 #pragma unroll
       for (int db = 0; db < nD; ++db) {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
-          dq[db] = mfma32(load_perm_k(st + Sm::kCols, Sm::cPitch, db * 32 + l32, 16 * cc, h), dsb[cc], dq[db]);
+          dq[db] = mfma32(tr_operand<D>(Ks, db, 16 * cc, lane), dsb[cc], dq[db]);
       }
     }
-    if (more) stash(smem + ((j + 1) & 1) * Sm::stageElems);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -368,19 +328,20 @@ hipError_t launch(const BwdArgs& a) {
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   const uint16_t* o = static_cast<const uint16_t*>(a.o);
   const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+  float* dvec = a.delta;
+  float* lse2 = a.delta + rows;
   constexpr int rpb = kThreads / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kThreads),
-                     0, a.stream, o, dout, a.delta, rows);
+                     0, a.stream, o, dout, a.lse, dvec, lse2, rows);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int nk = (a.T + kKeysPerWG - 1) / kKeysPerWG;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nk * BH), dim3(kThreads), 0, a.stream, q, k,
-                     v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk),
-                     static_cast<uint16_t*>(a.dv), a.T, BH, c, a.scale);
+                     v, dout, dvec, lse2, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv),
+                     a.T, BH, c, a.scale);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int nq = (a.T + kQueriesPerWG - 1) / kQueriesPerWG;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream, q, k,
-                     v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), a.T, BH, nq, c,
-                     a.scale);
+                     v, dout, dvec, lse2, static_cast<uint16_t*>(a.dq), a.T, BH, nq, c, a.scale);
   return hipGetLastError();
 }
 

@@ -63,10 +63,12 @@ struct FwdTile {
   static constexpr int stageBytes = 2 * tileBytes;      // K tile, then V tile
   static constexpr int loadsPerWave = kBlockN * CH / kThreads;  // 16-byte loads per lane per tensor
   static_assert(loadsPerWave * kThreads == kBlockN * CH, "tile split");
-  // XOR swizzle of the 16-byte chunks of a row, so that 16 lanes reading one
-  // logical chunk of 16 consecutive rows hit 16 different bank groups.
+  // XOR swizzle of the 16-byte chunks of a row. For D = 128 the row's low three bits go to
+  // chunk bits 1-3 and row bit 3 to chunk bit 0: 16 consecutive rows reading one logical
+  // chunk (the K operand) hit 16 different chunk positions, and the 8 rows x 4 chunks of a
+  // transposing V read cover every chunk position exactly twice.
   __device__ static __forceinline__ int swz(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : ((row >> 1) & 7);
   }
   __device__ static __forceinline__ int offset(int row, int lchunk) {
     return row * RB + ((lchunk ^ swz(row)) << 4);

@@ -21,7 +21,7 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *delta;  // (B, H, T) fp32 workspace
+  float *delta;  // workspace: D_i (B*H*T fp32), then LSE_i * log2(e) (B*H*T fp32)
   int B, H, T, D;
   float scale;
   bool causal;

@@ -91,8 +91,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (the D_i row
- * vector: 4*B*H*T bytes). Returns 0 if the sizes are invalid.
+ * Bytes of device workspace fa_bwd needs for these sizes: 8*B*H*T (the
+ * row vectors D_i = rowsum(dout * o) and LSE_i * log2(e), fp32 each).
+ * Returns 0 if the sizes are invalid.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int T, int D);
 

@@ -94,7 +94,7 @@ def test_bad_causal(lib):
 
 
 def test_bwd_workspace_bytes(lib):
-    assert lib.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 4 * 2 * 16 * 4096
+    assert lib.fa_bwd_workspace_bytes(2, 16, 4096, 128) == 8 * 2 * 16 * 4096
     assert lib.fa_bwd_workspace_bytes(0, 16, 4096, 128) == 0
     assert lib.fa_bwd_workspace_bytes(1, 1, 16, 96) == 0
 
@@ -112,4 +112,4 @@ def test_bwd_validation(lib):
     assert bwd(lib, dtype=0) == -4      # the backward is bf16 only
     assert bwd(lib, scale=-1.0) == -6
     assert bwd(lib, causal=5) == -7
-    assert bwd(lib, ws_bytes=63) == -7  # needs 4*B*H*T = 64 bytes
+    assert bwd(lib, ws_bytes=127) == -7  # needs 8*B*H*T = 128 bytes

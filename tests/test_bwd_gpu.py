@@ -127,15 +127,15 @@ def test_bwd_argument_errors(fa):
     x = torch.zeros(1, 1, 64, 64, device="cuda", dtype=torch.bfloat16)
     lse = torch.zeros(1, 1, 64, device="cuda")
     g = torch.full_like(x, 3.0)
-    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(512, dtype=torch.uint8, device="cuda")
     p = x.data_ptr()
 
-    def call(ws_bytes=256, dtype=1, D=64):
+    def call(ws_bytes=512, dtype=1, D=64):
         return lib.fa_bwd(p, p, p, p, p, lse.data_ptr(), g.data_ptr(), g.data_ptr(), g.data_ptr(),
                           ws.data_ptr(), ws_bytes, 1, 1, 64, D, ctypes.c_float(0.1), 1, dtype, None)
 
-    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 64) == 256
-    assert call(ws_bytes=255) == fa._lib.FA_ERR_ARG
+    assert lib.fa_bwd_workspace_bytes(1, 1, 64, 64) == 512
+    assert call(ws_bytes=511) == fa._lib.FA_ERR_ARG
     assert call(dtype=0) == fa._lib.FA_ERR_DTYPE
     assert call(D=96) == fa._lib.FA_ERR_HEADDIM
     torch.cuda.synchronize()
