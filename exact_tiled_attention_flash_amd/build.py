@@ -26,7 +26,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-fno-honor-nans", "-mno-amdgpu-ieee"]
 # per-source extra device flags
-EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", "-Wall",
           "-Wno-unused-function"]
 

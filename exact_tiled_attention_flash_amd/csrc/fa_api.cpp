@@ -13,6 +13,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;   // per tensor; keeps every offset in range
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,6 +23,8 @@ int check_sizes(int B, int H, int T, int D) {
   const int64_t bh = int64_t(B) * H;
   if (bh > INT32_MAX) return FA_ERR_SHAPE;
   if (bh * T * D > kMaxElems) return FA_ERR_SHAPE;
+  // one head of one tensor stays below 2^31 bytes: in-head offsets are 32-bit
+  if (int64_t(T) * D * 2 > kMaxHeadBytes) return FA_ERR_SHAPE;
   // the largest grid: one workgroup per 64 rows of every (b, h)
   if (bh * ((int64_t(T) + 63) / 64) > kMaxBlocks) return FA_ERR_SHAPE;
   return FA_OK;

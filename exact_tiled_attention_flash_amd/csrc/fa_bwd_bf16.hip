@@ -46,8 +46,8 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __res
                                                            float* __restrict__ L2, int64_t rows) {
   constexpr int LPR = D / 8;             // lanes per row, one 16-byte chunk each
   constexpr int RPB = kThreads / LPR;    // rows per workgroup
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int ch = threadIdx.x % LPR;
+  const int64_t row = (int64_t)workgroup_id() * RPB + lane_thread_id() / LPR;
+  const int ch = lane_thread_id() % LPR;
   float s = 0.f;
   if (row < rows) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + ch * 8);
@@ -108,13 +108,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   constexpr int nK = D / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * St::bytes];
 
-  const int tid = threadIdx.x;
+  const int tid = lane_thread_id();
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const int L = blockIdx.x;
+  const int L = workgroup_id();
   const int bh = L % BH;
   const int k0 = (L / BH) * kKeysPerWG;   // key tile 0 (the heaviest when causal) first
   const int kw0 = k0 + wave * 32;
@@ -228,13 +228,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   constexpr int stageBytes = 2 * Tl::bytes;   // K tile, then V tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * stageBytes];
 
-  const int tid = threadIdx.x;
+  const int tid = lane_thread_id();
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const int L = blockIdx.x;
+  const int L = workgroup_id();
   const int bh = L % BH;
   int qt = L / BH;
   if (CAUSAL) qt = nq - 1 - qt;  // longest key range first

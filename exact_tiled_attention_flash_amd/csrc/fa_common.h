@@ -20,6 +20,13 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Work-item and workgroup index straight from the hardware registers. The threadIdx /
+// blockIdx accessors go through device-library functions that are not inlined into code
+// built with -mno-amdgpu-ieee (mismatched function attributes); as calls they return the
+// workgroup index in a VGPR, so everything derived from it would be computed per lane.
+__device__ __forceinline__ int lane_thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int workgroup_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+
 // 32x32x16 bf16 matrix-core product, fp32 accumulate: acc += A(32x16) * B(16x32).
 // Operand lane layout: lane l supplies row/column (l % 32) and the 8 k-values of
 // k-half (l / 32). Result: lane l holds column (l % 32), rows

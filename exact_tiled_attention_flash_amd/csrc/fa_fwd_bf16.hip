@@ -1,50 +1,46 @@
 // Attention forward, bf16 storage, fp32 accumulation: hand-written gfx950 kernel.
 //
-// Method: "Lab 06 - Attention kernels", section 3 (per query tile keep the
-// row max m, row sum l and accumulator acc; per key tile rescale by
-// exp(m - m') and add exp(S - m') V; finish with O = acc / l and
-// LSE = m + log l; causal tiles above the diagonal are never loaded and only
-// diagonal tiles are masked element-wise) and section 5 (one program per
-// (query tile, batch*head)). "Triton FlashAttention-2 forward", "The kernel"
-// (queries outermost, P rounded to the input dtype before the P V product,
-// row sums in fp32, masked loads read zeros beyond T). Section 2 of the lab
-// page notes that subtracting any constant from the exponents and
-// multiplying back is exact; this kernel uses that freedom (see "lazy
-// rescale" below).
+// Method: "Lab 06 - Attention kernels", section 3 (per query tile keep the row max m, row
+// sum l and accumulator acc; per key tile rescale by exp(m - m') and add exp(S - m') V;
+// finish with O = acc / l and LSE = m + log l; causal tiles above the diagonal are never
+// loaded, diagonal tiles are masked element-wise) and section 5 (one program per
+// (query tile, batch*head)). "Triton FlashAttention-2 forward", "The kernel" (queries
+// outermost, P rounded to the input dtype before the P V product, masked loads read zeros
+// beyond T). Section 2 of the lab page: subtracting any constant from the exponents and
+// dividing it back out is exact, which the lazy reference below relies on.
 //
 // gfx950 mapping
-//   * Workgroup: 256 threads = 4 waves, one per SIMD; 256 queries of one
-//     (b, h), 64 per wave as two 32-query blocks. Every K / V operand read
-//     from LDS feeds two matrix-core products (one per query block), which
-//     halves LDS traffic per flop compared with 32 queries per wave; LDS
-//     bandwidth (128 B/clk/CU) is the limiter otherwise.
-//   * Key tiles of 64 are double-buffered in LDS; the global loads of tile
-//     j+1 are in flight while tile j is computed. K and V are stored
-//     row-major with padded pitches chosen for conflict-free reads.
-//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane: a
-//     row's 64 scores sit in 32 registers of lane l and 32 of lane l^32.
-//     The S^T accumulator layout is the B-operand layout of O^T += V^T P^T,
-//     so P never leaves registers. The V^T A operand comes straight from the
-//     row-major V tile through the transposing LDS read (ds_read_b64_tr_b16):
-//     within each 16-lane group, lane i addresses V[key0 + i/4][d0 + 4(i%4)]
-//     and lane j receives V[key0 .. key0+3][d0 + j].
+//   * Workgroup: 256 threads = 4 waves, one per SIMD; 256 queries of one (b, h), 64 per
+//     wave as two 32-query blocks. Every K / V operand read from LDS feeds two
+//     matrix-core products (one per query block), which halves LDS traffic per flop
+//     compared with 32 queries per wave.
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane: a row's 64 scores of
+//     a tile sit in 32 registers of lane l and 32 of lane l ^ 32. The S^T accumulator
+//     layout is the B-operand layout of O^T += V^T P^T, so P never leaves registers; the
+//     V^T A operand is a transposing LDS read (ds_read_b64_tr_b16) of the row-major tile.
+//   * K and V tiles (64 keys) reach LDS by direct HBM -> LDS loads into XOR-swizzled
+//     row-major tiles, two slots each; K runs one tile ahead of V (see the pipeline).
 //   * exp(x) is exp2(x * scale * log2 e): one FMA and one v_exp_f32.
-//   * Lazy rescale: a row's reference max is only moved (and acc, l
-//     rescaled) when the new tile max exceeds it by more than 2^8 in the
-//     exponent; otherwise P <= 2^8 is accumulated against the stale
-//     reference. acc / l is unchanged by the choice of reference, and the
-//     bound keeps every fp32 value far from overflow. The branch is taken
-//     on the first tile and rarely afterwards.
-//   * The loop over key tiles is split: tiles that need no mask run in a
-//     lean main loop; the causal diagonal tiles and the ragged last tile
-//     run in a masked tail, where fully hidden 32-query blocks are skipped.
-//   * Causal grid order is heaviest query tile first; consecutive workgroup
-//     ids walk (b, h) fastest, which keeps all tiles of one head on one XCD
-//     (workgroups are dealt to the 8 XCDs round-robin) so K and V of a head
-//     are shared through that XCD's L2.
+//   * Lazy reference: a row's reference max m_ref moves only when a tile max exceeds it by
+//     more than 2^8 in the exp2 domain (and on the first tile), so P <= 2^8 and the O^T
+//     accumulators are rescaled in a rare wave-uniform branch, never in the steady state.
+//     O is normalised by the sum of the bf16-rounded P that actually multiplied V, so a
+//     dominant key's rounding cancels between numerator and denominator; LSE uses the
+//     fp32 sum of the unrounded exponentials.
+//   * Software pipeline across key tiles, one wave: phase X of iteration j runs the S
+//     products of tile j+1 on the matrix cores while the VALU finishes tile j (the last
+//     exponentials, fp32 and rounded row sums, bf16 packing); phase Y runs tile j's
+//     P V products while the VALU takes tile j+1's row max, moves the references and
+//     starts its exponentials. Each step of a phase holds one matrix-core product and a
+//     fixed share of the VALU work, fenced with sched_barrier so the compiler keeps the
+//     interleaving.
+//   * Causal grid order is heaviest query tile first; consecutive workgroup ids walk
+//     (b, h) fastest, which keeps all tiles of one head on one XCD (workgroups are dealt
+//     to the 8 XCDs round-robin) so K and V of a head are shared through that XCD's L2.
 
 #include "fa_common.h"
 #include "fa_launch.h"
+#include "fa_swz.h"
 
 namespace fa {
 namespace {
@@ -52,90 +48,149 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBlockM = 256;   // queries per workgroup
 constexpr int kBlockN = 64;    // keys per tile
+// a row's reference max moves only when exceeded by more than 2^8 (in the exp2 domain)
+constexpr float kRescaleLog2 = 8.0f;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Matrix-core products with explicit register files. The O^T accumulators (128 registers
+// for D = 128) and the Q^T operands (64) live in AGPRs, which no VALU instruction touches
+// in the steady state; the S^T results and everything the VALU works on stay in VGPRs.
+// Written as inline asm because the compiler's own register-class choice either spills or
+// fails at this register pressure; the hazards the compiler would otherwise pad are
+// covered by the fences below, placed before any VALU access to a product's result.
+__device__ __forceinline__ void mfma_s_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// 20 wait states (more than the result latency of a 32x32x16 product) between the last
+// product writing x and y and any later instruction that uses them.
+__device__ __forceinline__ void fence2(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
+}
+template <int N>
+__device__ __forceinline__ void fence_acc(f32x16 (&a)[2][N]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < N; ++db) asm volatile("" : "+a"(a[qb][db]));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < N; ++db) asm volatile("" : "+a"(a[qb][db]));
+}
 
-template <int D>
-struct FwdTile {
-  static constexpr int CH = D / 8;                      // 16-byte chunks per row
-  static constexpr int RB = D * 2;                      // bytes per row (unpadded)
-  static constexpr int tileBytes = kBlockN * RB;        // one K or V tile
-  static constexpr int stageBytes = 2 * tileBytes;      // K tile, then V tile
-  static constexpr int loadsPerWave = kBlockN * CH / kThreads;  // 16-byte loads per lane per tensor
-  static_assert(loadsPerWave * kThreads == kBlockN * CH, "tile split");
-  // XOR swizzle of the 16-byte chunks of a row. For D = 128 the row's low three bits go to
-  // chunk bits 1-3 and row bit 3 to chunk bit 0: 16 consecutive rows reading one logical
-  // chunk (the K operand) hit 16 different chunk positions, and the 8 rows x 4 chunks of a
-  // transposing V read cover every chunk position exactly twice.
-  __device__ static __forceinline__ int swz(int row) {
-    return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : ((row >> 1) & 7);
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+// compile-time integer and loop: every step of a phase is generated as straight-line code
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(const F& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
   }
-  __device__ static __forceinline__ int offset(int row, int lchunk) {
-    return row * RB + ((lchunk ^ swz(row)) << 4);
-  }
+}
+// tile parity: selects the register buffers of a tile at compile time
+template <int P>
+struct Par {
+  static constexpr int value = P;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
+// v_permlane32_swap_b32 x, y: lanes 32-63 of x trade places with lanes 0-31 of y, so x
+// becomes [x_lo | y_lo] and y becomes [x_hi | y_hi]. Inline asm: with this toolchain the
+// builtin returns its first result for both results. Both swaps sit in one block between
+// s_nop padding: read before the VALU writes of its operands had reached every lane, the
+// swap returned stale upper lanes.
+__device__ __forceinline__ void permlane32_swap2(float& x, float& y, float& u, float& w) {
+  asm volatile(
+      "s_nop 7\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\ts_nop 7"
+      : "+v"(x), "+v"(y), "+v"(u), "+v"(w));
+}
 
-// Issue the direct global->LDS loads of key tile k0 (K and V) into `stage`.
-// Lane `lane` of load i of wave `wave` fills LDS bytes [16 u, 16 u + 16) of
-// the tile, u = (wave * loadsPerWave + i) * 64 + lane, i.e. physical chunk
-// u % CH of row u / CH; it fetches the logical chunk that the swizzle maps
-// there. Rows at or beyond T are clamped to row T - 1: such keys are masked
-// out of S and their V rows only ever meet P = 0.
+// Full-row maxima of two rows held as key halves in lanes l and l ^ 32 (a: query block 0,
+// b: query block 1): swap(a, b) puts row a's halves side by side in lanes 0-31 and row b's
+// in lanes 32-63, swap(b, a) the other way round.
+__device__ __forceinline__ void halves_max2(float& a, float& b, int h) {
+  float x = a, y = b, u = b, w = a;
+  permlane32_swap2(x, y, u, w);
+  const float f = fmaxf(x, y);   // lanes 0-31: row a, lanes 32-63: row b
+  const float g = fmaxf(u, w);   // lanes 0-31: row b, lanes 32-63: row a
+  a = h ? g : f;
+  b = h ? f : g;
+}
+
+// ---- per-step work assignment (all compile-time) --------------------------------------
+// Items of one tile: 64 score elements per lane, v = 32 qb + 16 kb + r; 8 chunks of 8
+// (v / 8 = 4 qb + cc, the B operand P[qb][cc]); 16 max items per key half (pairs of
+// elements). Query block 0 of a tile is finished in phase Y of the iteration before it is
+// used, query block 1 in phase X of its own iteration.
+// Item x of n items is done at step s0 + x (s1 - s0) / n of its window [s0, s1).
+constexpr int win_step(int x, int n, int s0, int s1) { return s0 + x * (s1 - s0) / n; }
+
 template <int D>
-__device__ __forceinline__ void issue_kv(uint8_t* stage, const uint16_t* __restrict__ Kh,
-                                         const uint16_t* __restrict__ Vh, int k0, int T,
-                                         int wave, int lane) {
-  using Tl = FwdTile<D>;
-#pragma unroll
-  for (int i = 0; i < Tl::loadsPerWave; ++i) {
-    const int slot = wave * Tl::loadsPerWave + i;
-    const int u = slot * 64 + lane;
-    const int row = u / Tl::CH;
-    const int lc = (u % Tl::CH) ^ Tl::swz(row);
-    const size_t g = (size_t)min(k0 + row, T - 1) * D + lc * 8;
-    __builtin_amdgcn_global_load_lds(Kh + g, (lds_void*)(stage + slot * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(Vh + g, (lds_void*)(stage + Tl::tileBytes + slot * 1024), 16,
-                                     0, 0);
+struct Sched {
+  static constexpr int nK = D / 16, nD = D / 32;
+  static constexpr int NX = 4 * nK;                  // phase X steps (S products)
+  static constexpr int NY = 8 * nD;                  // phase Y steps (P V products)
+  // phase Y: max over key half kb = 1, reference update, then query block 0's
+  // exponentials, sums and packing
+  static constexpr int YM0 = 2, YM1 = 2 + NY / 4, YR = YM1, YE0 = YR + 1, YE1 = NY - NY / 8;
+  static constexpr int YS0 = YE0 + 1, YS1 = NY;
+  // phase X: query block 1's exponentials, sums and packing, then the fold of the tile's
+  // sums; max over key half kb = 0 of the next tile once its products are done
+  static constexpr int XE0 = 0, XE1 = NX / 2, XS0 = 1, XS1 = NX / 2 + 4;
+  static constexpr int XM0 = NX / 2 + 2, XM1 = NX;
+  static constexpr int y_exp(int v) { return win_step(v, 32, YE0, YE1); }
+  static constexpr int y_sum(int v) { return win_step(v, 32, YS0, YS1); }
+  static constexpr int x_exp(int v) { return win_step(v - 32, 32, XE0, XE1); }
+  static constexpr int x_sum(int v) { return win_step(v - 32, 32, XS0, XS1); }
+  // a chunk is packed one step after its last exponential
+  static constexpr int y_pack(int ch) { return y_exp(8 * ch + 7) + 1; }
+  static constexpr int x_pack(int ch) { return x_exp(8 * ch + 7) + 1; }
+  static constexpr int XF = (x_sum(63) > x_pack(7) ? x_sum(63) : x_pack(7)) + 1;
+  static constexpr int x_max(int u) { return win_step(u, 16, XM0, XM1); }   // kb = 0
+  static constexpr int y_max(int u) { return win_step(u, 16, YM0, YM1); }   // kb = 1
+  // every sum and pack comes after the exponentials it reads, within its phase
+  static constexpr bool valid() {
+    for (int v = 0; v < 32; ++v)
+      if (y_sum(v) <= y_exp(v) || y_sum(v) >= NY || y_pack(v / 8) >= NY) return false;
+    for (int v = 32; v < 64; ++v)
+      if (x_sum(v) <= x_exp(v) || x_sum(v) >= NX) return false;
+    return YR < YE0 && XE1 <= NX && XF < NX && y_max(15) < YR;
   }
-}
-
-// A operand of O^T += V^T P^T for d rows [32 db, 32 db + 32) and keys 16 cc + {4h..4h+3,
-// 8+4h..8+4h+3}: two transposing reads from the row-major (swizzled) V tile.
-template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* Vs, int db, int cc, int lane) {
-  using Tl = FwdTile<D>;
-  const int g = lane >> 4, i = lane & 15;
-  const int key = 16 * cc + 4 * (g >> 1) + (i >> 2);
-  const int d0 = db * 32 + (g & 1) * 16 + 4 * (i & 3);
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(Vs + Tl::offset(key, d0 >> 3) + (d0 & 7) * 2));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(Vs + Tl::offset(key + 8, d0 >> 3) + (d0 & 7) * 2));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
+};
+static_assert(Sched<128>::valid() && Sched<64>::valid(), "pipeline schedule order");
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int T, int BH, int nq, float c) {
-  using Tl = FwdTile<D>;
+  using Tl = SwzTile<D>;
+  using S = Sched<D>;
   constexpr int nD = D / 32;   // 32-row blocks of O^T
   constexpr int nK = D / 16;   // k-steps of S^T
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * Tl::stageBytes];
+  constexpr int nKF = 2 * nK;  // K operand fragments per tile: f = nK kb + kk
+  constexpr int nVF = 4 * nD;  // V operand fragments per tile: g = nD cc + db
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * Tl::bytes];
 
-  const int tid = threadIdx.x;
+  const int tid = lane_thread_id();
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const int L = blockIdx.x;
+  const int L = workgroup_id();
   const int bh = L % BH;
   int qt = L / BH;
   if (CAUSAL) qt = nq - 1 - qt;
@@ -146,6 +201,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const uint16_t* Qh = Q + base;
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
+  auto kslot = [&](int t) { return smem + (t & 1) * Tl::bytes; };
+  auto vslot = [&](int t) { return smem + (2 + (t & 1)) * Tl::bytes; };
 
   // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
   // d = 16 kk + 8 h + 0..7.
@@ -160,131 +217,327 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       qf[qb][kk] = as_bf16x8(x);
     }
   }
+  // Move Q^T into AGPRs now and pad the accumulator writes before any product reads them.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
 
   const int kend = CAUSAL ? min(T, q0 + kBlockM) : T;
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
   // tiles [0, nfull) need no mask for any query of this workgroup
-  int nfull = (CAUSAL ? min(q0, T) : T) / kBlockN;
-  nfull = min(nfull, ntiles);
+  const int nfull = min((CAUSAL ? min(q0, T) : T) / kBlockN, ntiles);
 
   f32x16 acc[2][nD];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int db = 0; db < nD; ++db) acc[qb][db] = f32x16{};
-  float m_ref[2] = {kNegInf, kNegInf};   // running row max (raw score units)
-  float l_run[2] = {0.f, 0.f};           // partial row sums over this lane's key half
+  float m_ref[2], mc[2];            // reference max (raw score units) and m_ref * c
+  // row sums per (qb, key half kb): fp32 exponentials (l) and bf16-rounded P (r), for the
+  // tiles already folded in (lp, rp) and for the tile in progress (tl, tr), which may
+  // already use a newer reference
+  float lp[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, rp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  float tl[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, tr[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  float pm[2][2];                   // partial row maxima of the next tile, per (qb, kb)
+  // Scores -> exponentials and the bf16 P of a tile, per query block. Query block 0 of a
+  // tile is finished in the iteration before the tile's own, so its buffers are free again
+  // when the next tile's products start: one score buffer for block 0, two for block 1
+  // (tile parity); P of block 0 is double-buffered, P of block 1 single.
+  f32x16 s0[2], s1a[2], s1b[2];
+  bf16x8 p0a[4], p0b[4], p1[4];
+  // buffers of a tile of parity par: score block (qb, kb), P operand (qb, cc)
+  auto sblk = [&](auto par, int qb, int kb) -> f32x16& {
+    if constexpr (decltype(par)::value == 0) return qb ? s1a[kb] : s0[kb];
+    else return qb ? s1b[kb] : s0[kb];
+  };
+  auto pop = [&](auto par, int qb, int cc) -> bf16x8& {
+    if constexpr (decltype(par)::value == 0) return qb ? p1[cc] : p0a[cc];
+    else return qb ? p1[cc] : p0b[cc];
+  };
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  issue_kv<D>(smem, Kh, Vh, 0, T, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // Scores -> probabilities for one 32-query block; returns P^T as 4 bf16 B operands.
-  auto softmax_block = [&](f32x16 (&s)[2], int qb, bool masked, int k0, bf16x8 (&p)[4]) {
-    const int qrow = qw0 + 32 * qb + l32;
-    uint32_t valid = 0xffffffffu;
-    if (masked) {
-      valid = 0u;
+  // element (kb, r) of a lane is key 32 kb + 8 (r / 4) + (r % 4) + 4 h of the tile; it is
+  // valid for query block qb iff that local index is below lim[qb]
+  auto tile_lim = [&](int t, int (&lim)[2]) {
+    const int k0 = t * kBlockN;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool ok = key < T && (!CAUSAL || key <= qrow);
-          valid |= (ok ? 1u : 0u) << (16 * kb + r);
-          s[kb][r] = ok ? s[kb][r] : kNegInf;
-        }
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2)
-      mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_old = m_ref[qb];
-    const float m_new = fmaxf(m_old, mx);
-    // alpha = exp(m_old - m_new) (1 when the max did not move, 0 on the row's first tile)
-    const float alpha = (m_old == kNegInf) ? 0.f : exp2_fast((m_old - m_new) * c);
-    m_ref[qb] = m_new;
-    l_run[qb] *= alpha;
-#pragma unroll
-    for (int db = 0; db < nD; ++db) acc[qb][db] *= alpha;
-    const float mc = (m_new == kNegInf ? 0.f : m_new) * c;
-    float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float e = exp2_fast(fmaf(s[kb][r], c, -mc));
-        if (masked) e = (valid >> (16 * kb + r)) & 1u ? e : 0.f;
-        s[kb][r] = e;
-      }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ps0 += s[0][r];
-      ps1 += s[1][r];
-    }
-    l_run[qb] += ps0 + ps1;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const f32x16& sv = s[cc >> 1];
-      const int o = (cc & 1) * 8;
-      u32x4 w = {pack_bf16x2(sv[o + 0], sv[o + 1]), pack_bf16x2(sv[o + 2], sv[o + 3]),
-                 pack_bf16x2(sv[o + 4], sv[o + 5]), pack_bf16x2(sv[o + 6], sv[o + 7])};
-      p[cc] = as_bf16x8(w);
+    for (int qb = 0; qb < 2; ++qb) {
+      int l = T - k0;
+      if (CAUSAL) l = min(l, qw0 + 32 * qb + l32 - k0 + 1);
+      lim[qb] = l - 4 * h;
     }
   };
 
-  auto tile = [&](int j, bool masked) {
-    const int k0 = j * kBlockN;
-    const bool more = j + 1 < ntiles;
-    if (more) issue_kv<D>(smem + ((j + 1) & 1) * Tl::stageBytes, Kh, Vh, k0 + kBlockN, T, wave, lane);
-    const uint8_t* Ks = smem + (j & 1) * Tl::stageBytes;
-    const uint8_t* Vs = Ks + Tl::tileBytes;
-    // which 32-query blocks of this wave see any key of the tile
-    const bool act0 = !masked || !CAUSAL || k0 <= qw0 + 31;
-    const bool act1 = !masked || !CAUSAL || k0 <= qw0 + 63;
-    if (act1) {
-      f32x16 s0[2] = {f32x16{}, f32x16{}}, s1[2] = {f32x16{}, f32x16{}};
+  // ---- work items ------------------------------------------------------------------------
+  auto max_item = [&](auto par, int qb, int kb, int t, bool masked, const int (&lim)[2]) {
+    f32x16& x = sblk(par, qb, kb);
+    float a = x[2 * t], b = x[2 * t + 1];
+    if (masked) {
+      const int kla = 32 * kb + 8 * (t >> 1) + 2 * (t & 1);
+      a = kla < lim[qb] ? a : kNegInf;
+      b = kla + 1 < lim[qb] ? b : kNegInf;
+      x[2 * t] = a;
+      x[2 * t + 1] = b;
+    }
+    pm[qb][kb] = fmaxf(pm[qb][kb], fmaxf(a, b));
+  };
+  auto exp_item = [&](auto par, int v, bool masked) {
+    const int qb = v >> 5, kb = (v >> 4) & 1, r = v & 15;
+    f32x16& blk = sblk(par, qb, kb);
+    const float x = blk[r];
+    const float e = exp2_fast(fmaf(x, c, -mc[qb]));
+    blk[r] = (masked && x == kNegInf) ? 0.f : e;
+  };
+  auto sum_item = [&](auto par, int v) {
+    const int qb = v >> 5, kb = (v >> 4) & 1, r = v & 15;
+    tl[qb][kb] += sblk(par, qb, kb)[r];
+  };
+  // Pack chunk ch to the bf16 B operand and add the rounded values. The words are summed
+  // before they are gathered into the operand vector: with this toolchain,
+  // v_dot2c_f32_bf16 applied to an element of a 4-vector reads the vector's first register
+  // for the second element too.
+  auto pack_item = [&](auto spar, auto ppar, int ch) {
+    const int qb = ch >> 2, cc = ch & 3, kb = cc >> 1, o = (cc & 1) * 8;
+    const f32x16& sv = sblk(spar, qb, kb);
+    const uint32_t w0 = pack_bf16x2(sv[o + 0], sv[o + 1]), w1 = pack_bf16x2(sv[o + 2], sv[o + 3]);
+    const uint32_t w2 = pack_bf16x2(sv[o + 4], sv[o + 5]), w3 = pack_bf16x2(sv[o + 6], sv[o + 7]);
+    tr[qb][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, tr[qb][0], false);
+    tr[qb][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tr[qb][1], false);
+    tr[qb][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, tr[qb][0], false);
+    tr[qb][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, tr[qb][1], false);
+    pop(ppar, qb, cc) = as_bf16x8(u32x4{w0, w1, w2, w3});
+  };
+  // the finished tile's sums join the running sums (same reference by now)
+  auto fold = [&]() {
 #pragma unroll
-      for (int kk = 0; kk < nK; ++kk) {
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(Ks + Tl::offset(kb * 32 + l32, 2 * kk + h)));
-          if (act0) s0[kb] = mfma32(a, qf[0][kk], s0[kb]);
-          s1[kb] = mfma32(a, qf[1][kk], s1[kb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        lp[qb][kb] += tl[qb][kb];
+        rp[qb][kb] += tr[qb][kb];
+        tl[qb][kb] = 0.f;
+        tr[qb][kb] = 0.f;
       }
-      bf16x8 p0[4], p1[4];
-      const bool mask0 = masked && (k0 + kBlockN > T || (CAUSAL && k0 + kBlockN - 1 > qw0));
-      const bool mask1 = masked && (k0 + kBlockN > T || (CAUSAL && k0 + kBlockN - 1 > qw0 + 32));
-      if (act0) softmax_block(s0, 0, mask0, k0, p0);
-      softmax_block(s1, 1, mask1, k0, p1);
+  };
+  // Full-row maxima of the next tile; moves the references (all rows of the wave together,
+  // when any row exceeds its reference by more than the margin) and returns whether the
+  // folded sums and the accumulators need the rescale by exp(m_old - m_ref).
+  auto reduce = [&](float (&m_old)[2]) {
+    float a = fmaxf(pm[0][0], pm[0][1]), b = fmaxf(pm[1][0], pm[1][1]);
+    halves_max2(a, b, h);
+    const bool need = (a - m_ref[0]) * c > kRescaleLog2 || (b - m_ref[1]) * c > kRescaleLog2;
+    const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+    m_old[0] = m_ref[0];
+    m_old[1] = m_ref[1];
+    m_ref[0] = any ? fmaxf(m_ref[0], a) : m_ref[0];
+    m_ref[1] = any ? fmaxf(m_ref[1], b) : m_ref[1];
+    mc[0] = m_ref[0] * c;
+    mc[1] = m_ref[1] * c;
+    return any;
+  };
+  auto rescale = [&](const float (&m_old)[2]) {
 #pragma unroll
-      for (int db = 0; db < nD; ++db) {
+    for (int qb = 0; qb < 2; ++qb) {
+      const float alpha = exp2_fast((m_old[qb] - m_ref[qb]) * c);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16x8 a = v_operand<D>(Vs, db, cc, lane);
-          if (act0) acc[0][db] = mfma32(a, p0[cc], acc[0][db]);
-          acc[1][db] = mfma32(a, p1[cc], acc[1][db]);
-        }
+      for (int db = 0; db < nD; ++db) acc[qb][db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        lp[qb][kb] *= alpha;
+        rp[qb][kb] *= alpha;
       }
     }
-    // the next tile's loads (this wave's) have landed; the barrier makes every
-    // wave's part visible and frees this stage for the loads of tile j + 2
+  };
+  auto reset_max = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) pm[qb][0] = pm[qb][1] = kNegInf;
+  };
+  auto k_frag = [&](const uint8_t* Ks, int f) {
+    return row_operand<D>(Ks, (f / nK) * 32 + l32, 2 * (f % nK) + h);
+  };
+  auto v_frag = [&](const uint8_t* Vs, int g) { return tr_operand<D>(Vs, g % nD, 16 * (g / nD), lane); };
+
+  // ---- one pipelined iteration: tile j finishes, tile j+1 starts --------------------------
+  // On entry: query block 0 of tile j is exponentiated, summed (tl, tr) and packed (pc);
+  // cur holds query block 1's scores; tile j+1's K is in kslot(j+1), tile j's V in vslot(j).
+  // cur / nxt: parity tags of tile j and tile j+1
+  auto iteration = [&](auto cur, auto nxt, int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;   // tile j or j+1 may need masks
+    if (j + 2 < ntiles) issue_tile<D>(kslot(j + 2), Kh, (j + 2) * kBlockN, T, wave, lane);
+    issue_tile<D>(vslot(j + 1), Vh, (j + 1) * kBlockN, T, wave, lane);
+    int lim[2];
+    if (MASK) tile_lim(j + 1, lim);
+    const uint8_t* Kn = kslot(j + 1);
+    const uint8_t* Vs = vslot(j);
+    reset_max();
+
+    // phase X: S of tile j+1 | query block 1 of tile j
+    bf16x8 kf[nKF];
+    kf[0] = k_frag(Kn, 0);
+    kf[1] = k_frag(Kn, 1);
+    bf16x8 vf[nVF];
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, S::NX>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int f = i >> 1, qb = i & 1, kb = f / nK, kk = f % nK;
+      if constexpr (qb == 0 && f + 2 < nKF) kf[f + 2] = k_frag(Kn, f + 2);
+      if constexpr (i == S::NX - 2) {
+        vf[0] = v_frag(Vs, 0);
+        vf[1] = v_frag(Vs, 1);
+      }
+      if constexpr (kk == 0) mfma_s_first(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
+      else mfma_s(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
+      if constexpr (i == S::XM0) fence2(sblk(nxt, 0, 0), sblk(nxt, 1, 0));
+      static_for<32, 64>([&](auto vc) {
+        constexpr int v = decltype(vc)::value;
+        if constexpr (S::x_exp(v) == i) exp_item(cur, v, MASK);
+        if constexpr (S::x_sum(v) == i) sum_item(cur, v);
+      });
+      static_for<4, 8>([&](auto cc_) {
+        constexpr int ch = decltype(cc_)::value;
+        if constexpr (S::x_pack(ch) == i) pack_item(cur, cur, ch);
+      });
+      if constexpr (i == S::XF) fold();
+      static_for<0, 16>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (S::x_max(u) == i) max_item(nxt, u >> 3, 0, u & 7, MASK, lim);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // phase Y: P V of tile j | max, reference update and query block 0 of tile j+1
+    float m_old[2];
+    bool any = false;
+    static_for<0, S::NY>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int g = i >> 1, qb = i & 1, cc = g / nD, db = g % nD;
+      if constexpr (qb == 0 && g + 2 < nVF) vf[g + 2] = v_frag(Vs, g + 2);
+      mfma_o(acc[qb][db], vf[g], pop(cur, qb, cc));
+      if constexpr (i == S::YM0) fence2(sblk(nxt, 0, 1), sblk(nxt, 1, 1));
+      static_for<0, 16>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (S::y_max(u) == i) max_item(nxt, u >> 3, 1, u & 7, MASK, lim);
+      });
+      if constexpr (i == S::YR) any = reduce(m_old);
+      static_for<0, 32>([&](auto vc) {
+        constexpr int v = decltype(vc)::value;
+        if constexpr (S::y_exp(v) == i) exp_item(nxt, v, MASK);
+        if constexpr (S::y_sum(v) == i) sum_item(nxt, v);
+      });
+      static_for<0, 4>([&](auto cc_) {
+        constexpr int ch = decltype(cc_)::value;
+        if constexpr (S::y_pack(ch) == i) pack_item(nxt, nxt, ch);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (any) {
+      fence_acc(acc);
+      rescale(m_old);
+    }
+    // this wave's loads of K j+2 and V j+1 have landed; the barrier publishes every wave's
+    // part and retires kslot(j+1) and vslot(j)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
-  for (int j = 0; j < nfull; ++j) tile(j, false);
-  for (int j = nfull; j < ntiles; ++j) tile(j, true);
+  // ---- last tile: finish query block 1 and multiply (no next tile) -------------------------
+  auto last = [&](auto cur, int j) {
+    const uint8_t* Vs = vslot(j);
+#pragma unroll
+    for (int v = 32; v < 64; ++v) exp_item(cur, v, true);
+#pragma unroll
+    for (int v = 32; v < 64; ++v) sum_item(cur, v);
+#pragma unroll
+    for (int ch = 4; ch < 8; ++ch) pack_item(cur, cur, ch);
+    fold();
+    // the products below read P right after the VALU wrote it
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p1[0]), "+v"(p1[1]), "+v"(p1[2]), "+v"(p1[3]));
+#pragma unroll
+    for (int g = 0; g < nVF; ++g) {
+      const bf16x8 a = v_frag(Vs, g);
+      const int cc = g / nD, db = g % nD;
+      mfma_o(acc[0][db], a, pop(cur, 0, cc));
+      mfma_o(acc[1][db], a, pop(cur, 1, cc));
+    }
+  };
 
+  // ---- prologue: tile 0's scores, max and query block 0 ---------------------------------
+  issue_tile<D>(kslot(0), Kh, 0, T, wave, lane);
+  issue_tile<D>(vslot(0), Vh, 0, T, wave, lane);
+  if (ntiles > 1) issue_tile<D>(kslot(1), Kh, kBlockN, T, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  {
+    const uint8_t* K0 = kslot(0);
+#pragma unroll
+    for (int f = 0; f < nKF; ++f) {
+      const bf16x8 a = k_frag(K0, f);
+      const int kb = f / nK, kk = f % nK;
+      if (kk == 0) {
+        mfma_s_first(s0[kb], a, qf[0][kk]);
+        mfma_s_first(s1a[kb], a, qf[1][kk]);
+      } else {
+        mfma_s(s0[kb], a, qf[0][kk]);
+        mfma_s(s1a[kb], a, qf[1][kk]);
+      }
+    }
+    fence2(s0[0], s1a[0]);
+    fence2(s0[1], s1a[1]);
+    const bool masked = nfull == 0;
+    int lim[2];
+    tile_lim(0, lim);
+    reset_max();
+#pragma unroll
+    for (int u = 0; u < 32; ++u) max_item(Par<0>{}, u >> 4, (u >> 3) & 1, u & 7, masked, lim);
+    float a = fmaxf(pm[0][0], pm[0][1]), b = fmaxf(pm[1][0], pm[1][1]);
+    halves_max2(a, b, h);
+    // every row sees key 0, so both maxima are finite
+    m_ref[0] = a;
+    m_ref[1] = b;
+    mc[0] = a * c;
+    mc[1] = b * c;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) exp_item(Par<0>{}, v, masked);
+#pragma unroll
+    for (int v = 0; v < 32; ++v) sum_item(Par<0>{}, v);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) pack_item(Par<0>{}, Par<0>{}, ch);
+  }
+  // every wave is done with kslot(0) before iteration 0 refills it
+  __syncthreads();
+
+  int j = 0;
+  for (; j + 2 < nfull; j += 2) {
+    iteration(Par<0>{}, Par<1>{}, j, Flag<false>{});
+    iteration(Par<1>{}, Par<0>{}, j + 1, Flag<false>{});
+  }
+  // masked tail (at most five tiles): one body, the next tile's block-1 scores and block-0
+  // P are moved into the even buffers after each iteration so the roles never alternate
+  for (; j + 1 < ntiles; ++j) {
+    iteration(Par<0>{}, Par<1>{}, j, Flag<true>{});
+    s1a[0] = s1b[0];
+    s1a[1] = s1b[1];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) p0a[cc] = p0b[cc];
+  }
+  last(Par<0>{}, j);
+
+  fence_acc(acc);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = qw0 + 32 * qb + l32;
-    const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+    const float l_half = lp[qb][0] + lp[qb][1];
+    const float r_half = rp[qb][0] + rp[qb][1];
+    const float l_tot = l_half + swap_halves(l_half);
+    const float r_tot = r_half + swap_halves(r_half);
     if (qrow < T) {
-      const float inv = 1.0f / l_tot;
+      const float inv = 1.0f / r_tot;
       uint16_t* orow = O + base + (size_t)qrow * D;
 #pragma unroll
       for (int db = 0; db < nD; ++db) {

@@ -73,13 +73,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
   constexpr int nD = D / 32;
   __shared__ __attribute__((aligned(16))) float smem[2 * Tl::stageElems];
 
-  const int tid = threadIdx.x;
+  const int tid = lane_thread_id();
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const int L = blockIdx.x;
+  const int L = workgroup_id();
   const int bh = L % BH;
   int qt = L / BH;
   if (CAUSAL) qt = nq - 1 - qt;

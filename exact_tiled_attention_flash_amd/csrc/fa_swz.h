@@ -43,8 +43,10 @@ __device__ __forceinline__ void issue_tile(uint8_t* dst, const uint16_t* __restr
     const int u = slot * 64 + lane;
     const int row = u / Tl::CH;
     const int lc = (u % Tl::CH) ^ Tl::swz(row);
-    const size_t g = (size_t)min(row0 + row, T - 1) * D + lc * 8;
-    __builtin_amdgcn_global_load_lds(src + g, (lds_void*)(dst + slot * 1024), 16, 0, 0);
+    // 32-bit byte offset from the wave-uniform base (one head is below 2^31 bytes)
+    const uint32_t off = (uint32_t)(min(row0 + row, T - 1) * D + lc * 8) * 2u;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + off,
+                                     (lds_void*)(dst + slot * 1024), 16, 0, 0);
   }
 }
 

@@ -62,7 +62,8 @@ enum fa_dtype {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,      /* a required pointer is NULL */
-    FA_ERR_SHAPE = -2,     /* B, H or T < 1, or the sizes overflow the index range */
+    FA_ERR_SHAPE = -2,     /* B, H or T < 1, the sizes overflow the index range, or one
+                              head of one tensor (T * D elements) reaches 2^31 bytes */
     FA_ERR_HEADDIM = -3,   /* D is not 64 or 128 */
     FA_ERR_DTYPE = -4,     /* dtype is not a supported fa_dtype for this call */
     FA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */

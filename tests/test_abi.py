@@ -69,6 +69,14 @@ def test_bad_shapes(lib, B, H, T):
     assert fwd(lib, B=B, H=H, T=T) == -2
 
 
+def test_head_size_bound(lib):
+    # one head of one tensor must stay below 2^31 bytes (in-head offsets are 32-bit)
+    assert fwd(lib, B=1, H=1, T=1 << 23, D=128) == -2
+    assert fwd(lib, B=1, H=1, T=1 << 24, D=64) == -2
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1 << 23, 128) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, (1 << 23) - 1, 128) == 8 * ((1 << 23) - 1)
+
+
 @pytest.mark.parametrize("D", [0, 32, 96, 256, 127])
 def test_bad_head_dim(lib, D):
     assert fwd(lib, D=D) == -3
