@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * St::bytes];
 
   const int tid = lane_thread_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -140,10 +140,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int nqt = (T + kQTile - 1) / kQTile;
   const int qt0 = CAUSAL ? k0 / kQTile : 0;
 
+  const TileLoader<D> ld(wave, lane);
   auto fetch = [&](int qt, uint8_t* st) {
     const int q0 = qt * kQTile;
-    issue_tile<D>(st + St::q, Q + base, q0, T, wave, lane);
-    issue_tile<D>(st + St::dO, dO + base, q0, T, wave, lane);
+    ld.issue_all(st + St::q, Q + base, q0, T);
+    ld.issue_all(st + St::dO, dO + base, q0, T);
     if (wave == 0) issue_stats(st + St::lse2, L2 + rbase, q0, T, lane);
     if (wave == 1) issue_stats(st + St::dvec, Dv + rbase, q0, T, lane);
   };
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * stageBytes];
 
   const int tid = lane_thread_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -260,9 +261,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(T, q0 + kQueriesPerWG) : T;
   const int ntiles = (kend + kKTile - 1) / kKTile;
 
+  const TileLoader<D> ld(wave, lane);
   auto fetch = [&](int j, uint8_t* st) {
-    issue_tile<D>(st, K + base, j * kKTile, T, wave, lane);
-    issue_tile<D>(st + Tl::bytes, V + base, j * kKTile, T, wave, lane);
+    ld.issue_all(st, K + base, j * kKTile, T);
+    ld.issue_all(st + Tl::bytes, V + base, j * kKTile, T);
   };
   fetch(0, smem);
   __builtin_amdgcn_s_waitcnt(0);

@@ -26,6 +26,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 // workgroup index in a VGPR, so everything derived from it would be computed per lane.
 __device__ __forceinline__ int lane_thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
 __device__ __forceinline__ int workgroup_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+// index of this wave in its workgroup, as a wave-uniform (scalar) value
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(lane_thread_id() >> 6);
+}
 
 // 32x32x16 bf16 matrix-core product, fp32 accumulate: acc += A(32x16) * B(16x32).
 // Operand lane layout: lane l supplies row/column (l % 32) and the 8 k-values of

@@ -182,10 +182,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   constexpr int nK = D / 16;   // k-steps of S^T
   constexpr int nKF = 2 * nK;  // K operand fragments per tile: f = nK kb + kk
   constexpr int nVF = 4 * nD;  // V operand fragments per tile: g = nD cc + db
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * Tl::bytes];
+  // Two slots per tensor, each its own LDS object: where the slot parity is known at compile
+  // time the compiler can tell a slot being refilled by DMA from the one being read, and
+  // need not wait for the DMA before every LDS read.
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[Tl::bytes], ks1[Tl::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[Tl::bytes], vs1[Tl::bytes];
 
   const int tid = lane_thread_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -201,8 +205,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const uint16_t* Qh = Q + base;
   const uint16_t* Kh = K + base;
   const uint16_t* Vh = V + base;
-  auto kslot = [&](int t) { return smem + (t & 1) * Tl::bytes; };
-  auto vslot = [&](int t) { return smem + (2 + (t & 1)) * Tl::bytes; };
+  auto kslot = [&](int t) -> uint8_t* { return (t & 1) ? ks1 : ks0; };
+  auto vslot = [&](int t) -> uint8_t* { return (t & 1) ? vs1 : vs0; };
+  // jp: parity of j as IC<0> / IC<1>, or IC<-1> when only known at run time
+  auto kslot_p = [&](auto jp, int j, int d) -> uint8_t* {
+    constexpr int P = decltype(jp)::value;
+    if constexpr (P < 0) return kslot(j + d);
+    else return ((P + d) & 1) ? ks1 : ks0;
+  };
+  auto vslot_p = [&](auto jp, int j, int d) -> uint8_t* {
+    constexpr int P = decltype(jp)::value;
+    if constexpr (P < 0) return vslot(j + d);
+    else return ((P + d) & 1) ? vs1 : vs0;
+  };
+  const TileLoader<D> ld(wave, lane);
 
   // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
   // d = 16 kk + 8 h + 0..7.
@@ -367,14 +383,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // On entry: query block 0 of tile j is exponentiated, summed (tl, tr) and packed (pc);
   // cur holds query block 1's scores; tile j+1's K is in kslot(j+1), tile j's V in vslot(j).
   // cur / nxt: parity tags of tile j and tile j+1
-  auto iteration = [&](auto cur, auto nxt, int j, auto mask_tag) {
+  auto iteration = [&](auto cur, auto nxt, int j, auto mask_tag, auto jp) {
     constexpr bool MASK = decltype(mask_tag)::value;   // tile j or j+1 may need masks
-    if (j + 2 < ntiles) issue_tile<D>(kslot(j + 2), Kh, (j + 2) * kBlockN, T, wave, lane);
-    issue_tile<D>(vslot(j + 1), Vh, (j + 1) * kBlockN, T, wave, lane);
     int lim[2];
     if (MASK) tile_lim(j + 1, lim);
-    const uint8_t* Kn = kslot(j + 1);
-    const uint8_t* Vs = vslot(j);
+    const uint8_t* Kn = kslot_p(jp, j, 1);
+    const uint8_t* Vs = vslot_p(jp, j, 0);
     reset_max();
 
     // phase X: S of tile j+1 | query block 1 of tile j
@@ -387,6 +401,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       constexpr int i = decltype(ic)::value;
       constexpr int f = i >> 1, qb = i & 1, kb = f / nK, kk = f % nK;
       if constexpr (qb == 0 && f + 2 < nKF) kf[f + 2] = k_frag(Kn, f + 2);
+      // loads of K j+2 and V j+1, one per odd step (K j+2 is clamped into range past the last
+      // tile: a harmless reload into a slot nobody reads any more)
+      if constexpr ((i & 1) && (i >> 1) < Tl::loadsPerWave)
+        ld.issue(kslot_p(jp, j, 2), Kh, (j + 2) * kBlockN, T, i >> 1);
+      if constexpr ((i & 1) && (i >> 1) >= Tl::loadsPerWave && (i >> 1) < 2 * Tl::loadsPerWave)
+        ld.issue(vslot_p(jp, j, 1), Vh, (j + 1) * kBlockN, T, (i >> 1) - Tl::loadsPerWave);
       if constexpr (i == S::NX - 2) {
         vf[0] = v_frag(Vs, 0);
         vf[1] = v_frag(Vs, 1);
@@ -468,9 +488,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   };
 
   // ---- prologue: tile 0's scores, max and query block 0 ---------------------------------
-  issue_tile<D>(kslot(0), Kh, 0, T, wave, lane);
-  issue_tile<D>(vslot(0), Vh, 0, T, wave, lane);
-  if (ntiles > 1) issue_tile<D>(kslot(1), Kh, kBlockN, T, wave, lane);
+  ld.issue_all(kslot(0), Kh, 0, T);
+  ld.issue_all(vslot(0), Vh, 0, T);
+  if (ntiles > 1) ld.issue_all(kslot(1), Kh, kBlockN, T);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   {
@@ -514,13 +534,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   int j = 0;
   for (; j + 2 < nfull; j += 2) {
-    iteration(Par<0>{}, Par<1>{}, j, Flag<false>{});
-    iteration(Par<1>{}, Par<0>{}, j + 1, Flag<false>{});
+    iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
+    iteration(Par<1>{}, Par<0>{}, j + 1, Flag<false>{}, IC<1>{});
   }
   // masked tail (at most five tiles): one body, the next tile's block-1 scores and block-0
   // P are moved into the even buffers after each iteration so the roles never alternate
   for (; j + 1 < ntiles; ++j) {
-    iteration(Par<0>{}, Par<1>{}, j, Flag<true>{});
+    iteration(Par<0>{}, Par<1>{}, j, Flag<true>{}, IC<-1>{});
     s1a[0] = s1b[0];
     s1a[1] = s1b[1];
 #pragma unroll

@@ -10,9 +10,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// A [64 x D] bf16 tile stored unpadded; the 16-byte chunks of a row are XOR-swizzled so that
-// (a) 16 lanes reading one logical chunk of 16 consecutive rows, and (b) a transposing read
-// covering 8 consecutive rows x 4 chunks, spread evenly over the LDS banks.
+// A [64 x D] bf16 tile stored unpadded; the 16-byte chunks of a row are XOR-swizzled. Two
+// read patterns must spread over the LDS banks: (a) a 16-byte read by lanes holding
+// consecutive rows of one logical chunk (8 rows per LDS cycle with 32 four-byte banks, 16
+// with 64), and (b) a transposing read, whose 16-lane groups cover 4 consecutive rows x 2
+// adjacent chunks (x 4 chunks per cycle with 64 banks). For D = 128 the swizzle maps row bits
+// (0, 1, 2, 1^3) to chunk bits (2, 3, 0, 1): any aligned 8 (16) rows land on distinct chunks
+// modulo 8 (16), and any aligned 4 rows differ in chunk bits 1-2 and in bits 2-3, which
+// keeps both patterns conflict-free for either bank count.
 template <int D>
 struct SwzTile {
   static constexpr int CH = D / 8;                     // 16-byte chunks per row
@@ -21,34 +26,50 @@ struct SwzTile {
   static constexpr int loadsPerWave = 64 * CH / 256;   // 16-byte loads per lane (4 waves)
   static_assert(loadsPerWave * 256 == 64 * CH, "tile split");
   __device__ static __forceinline__ int swz(int row) {
-    return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : ((row >> 1) & 7);
+    return D == 128 ? (((row & 3) << 2) | ((((row >> 1) ^ (row >> 3)) & 1) << 1) | ((row >> 2) & 1))
+                    : ((row >> 1) & 7);
   }
   __device__ static __forceinline__ int offset(int row, int lchunk) {
     return row * RB + ((lchunk ^ swz(row)) << 4);
   }
 };
 
-// Direct HBM -> LDS load of rows [row0, row0 + 64) of a (rows x D) matrix by the 4 waves of
-// a workgroup. Lane `lane` of load i of wave `wave` fills tile bytes [16 u, 16 u + 16),
+// Direct HBM -> LDS loads of 64-row tiles of a (rows x D) matrix by the 4 waves of a
+// workgroup. Lane `lane` of load i of wave `wave` fills tile bytes [16 u, 16 u + 16),
 // u = (wave * loadsPerWave + i) * 64 + lane, i.e. physical chunk u % CH of row u / CH, with
-// the logical chunk the swizzle maps there. Rows at or beyond T are clamped to row T - 1;
-// callers mask or never store whatever depends on them.
+// the logical chunk the swizzle maps there. The lane's rows and in-row byte offsets do not
+// depend on the tile and are computed once; per load only the row clamp and one multiply-add
+// remain. Rows at or beyond T are clamped to row T - 1; callers mask or never store
+// whatever depends on them. `wave` must be wave-uniform (it selects the LDS destination).
 template <int D>
-__device__ __forceinline__ void issue_tile(uint8_t* dst, const uint16_t* __restrict__ src, int row0,
-                                           int T, int wave, int lane) {
+struct TileLoader {
   using Tl = SwzTile<D>;
+  int row[Tl::loadsPerWave];        // tile row of the lane's i-th chunk
+  uint32_t cofs[Tl::loadsPerWave];  // byte offset of that chunk within its row
+  int wave;
+  __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
 #pragma unroll
-  for (int i = 0; i < Tl::loadsPerWave; ++i) {
-    const int slot = wave * Tl::loadsPerWave + i;
-    const int u = slot * 64 + lane;
-    const int row = u / Tl::CH;
-    const int lc = (u % Tl::CH) ^ Tl::swz(row);
-    // 32-bit byte offset from the wave-uniform base (one head is below 2^31 bytes)
-    const uint32_t off = (uint32_t)(min(row0 + row, T - 1) * D + lc * 8) * 2u;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + off,
-                                     (lds_void*)(dst + slot * 1024), 16, 0, 0);
+    for (int i = 0; i < Tl::loadsPerWave; ++i) {
+      const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
+      row[i] = u / Tl::CH;
+      cofs[i] = (uint32_t)(((u % Tl::CH) ^ Tl::swz(row[i])) * 16);
+    }
   }
-}
+  // load i of rows [row0, row0 + 64) of src into the tile at dst
+  __device__ __forceinline__ void issue(uint8_t* dst, const uint16_t* __restrict__ src, int row0,
+                                        int T, int i) const {
+    // 32-bit byte offset from the wave-uniform base (one head is below 2^31 bytes)
+    const uint32_t off = (uint32_t)min(row0 + row[i], T - 1) * (uint32_t)(D * 2) + cofs[i];
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + off,
+                                     (lds_void*)(dst + (wave * Tl::loadsPerWave + i) * 1024), 16,
+                                     0, 0);
+  }
+  __device__ __forceinline__ void issue_all(uint8_t* dst, const uint16_t* __restrict__ src, int row0,
+                                            int T) const {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, src, row0, T, i);
+  }
+};
 
 // 16-byte operand fragment: 8 bf16 of row `row`, logical chunk `lchunk`.
 template <int D>
