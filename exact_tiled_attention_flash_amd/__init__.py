@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     fa_bwd,
     fa_bwd_workspace_bytes,
     fa_fwd,
+    fa_fwd_gqa,
+    fa_fwd_varlen,
     fa_status_string,
     load_library,
 )

@@ -46,6 +46,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_status_string.argtypes = [i]
     lib.fa_fwd.restype = i
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_gqa.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     if hasattr(lib, "fa_bwd"):
         lib.fa_bwd.restype = i
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -113,6 +117,75 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
         raise ValueError("lse must be a contiguous float32 (B, H, T) tensor")
     rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                     B, H, T, D, float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, l
+
+
+def _check_plain(name: str, t: torch.Tensor, dtype: torch.dtype, dims: int):
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or t.dim() != dims:
+        raise ValueError(f"{name} must be a contiguous {dims}-d {dtype} device tensor")
+
+
+def fa_fwd_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+               scale: float | None = None, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None):
+    """Grouped K/V heads and separate lengths: q (B, Hq, Tq, D), k and v (B, Hkv, Tk, D),
+    bf16; query head h uses K/V head h // (Hq // Hkv). Causal is aligned at the bottom right.
+    Returns o (B, Hq, Tq, D) and lse (B, Hq, Tq) float32. Enqueued on the current stream."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_plain(name, t, torch.bfloat16, 4)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be (B, Hkv, Tk, D) with q's B and D")
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_plain("out", o, torch.bfloat16, 4)
+    _check_plain("lse", l, torch.float32, 3)
+    if o.shape != q.shape or tuple(l.shape) != (B, Hq, Tq):
+        raise ValueError("out must match q and lse must be (B, Hq, Tq)")
+    rc = lib.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                        B, Hq, Hkv, Tq, Tk, D, float(scale), int(bool(causal)), FA_BF16, _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, l
+
+
+def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int, causal: bool = False,
+                  scale: float | None = None, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | None = None):
+    """Packed batch: q (total_q, Hq, D), k and v (total_k, Hkv, D), bf16; cu_seqlens_q / _k
+    int32 device tensors of B + 1 offsets. Returns o (total_q, Hq, D) and lse (Hq, total_q)
+    float32. Enqueued on the current stream."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_plain(name, t, torch.bfloat16, 3)
+    _check_plain("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    _check_plain("cu_seqlens_k", cu_seqlens_k, torch.int32, 1)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    if k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("k and v must be (total_k, Hkv, D) with q's D")
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_plain("out", o, torch.bfloat16, 3)
+    _check_plain("lse", l, torch.float32, 2)
+    if o.shape != q.shape or tuple(l.shape) != (Hq, total_q):
+        raise ValueError("out must match q and lse must be (Hq, total_q)")
+    rc = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                           cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q,
+                           total_k, int(max_seqlen_q), D, float(scale), int(bool(causal)), FA_BF16,
+                           _stream(q))
     if rc != FA_OK:
         raise FaError(rc)
     return o, l

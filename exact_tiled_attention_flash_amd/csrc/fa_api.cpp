@@ -30,6 +30,20 @@ int check_sizes(int B, int H, int T, int D) {
   return FA_OK;
 }
 
+// Sizes of the grouped / cross-length / packed forward: Hq = G * Hkv, and the rows of one
+// head of every tensor (Tq or Tk rows of `rs` elements) below 2^31 bytes.
+int check_sizes_general(int B, int Hq, int Hkv, int Tq, int Tk, int D, int q_rs, int kv_rs) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 1 || Tk < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+  if (int64_t(B) * Hq * Tq * D > kMaxElems || int64_t(B) * Hkv * Tk * D > kMaxElems) return FA_ERR_SHAPE;
+  if (int64_t(Tq) * q_rs * 2 > kMaxHeadBytes || int64_t(Tk) * kv_rs * 2 > kMaxHeadBytes) return FA_ERR_SHAPE;
+  if (int64_t(B) * Hq * ((int64_t(Tq) + 63) / 64) > kMaxBlocks) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 int check_scale(float scale) {
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   return FA_OK;
@@ -70,6 +84,40 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                 static_cast<hipStream_t>(stream)};
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a) : fa::launch_fwd_f32(a);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int Tq, int Tk, int D, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (int rc = check_sizes_general(B, Hq, Hkv, Tq, Tk, D, D, D)) return rc;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const fa::FwdBf16Problem p{q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, D, Tq, Tk, Tq,
+                             scale, causal != 0, static_cast<hipStream_t>(stream)};
+  return fa::launch_fwd_bf16_general(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                  int total_q, int total_k, int max_seqlen_q, int D, float scale, int causal,
+                  int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  if (max_seqlen_q < 1 || max_seqlen_q > total_q) return FA_ERR_SHAPE;
+  if (int rc = check_sizes_general(1, Hq, Hkv, total_q, total_k, D, Hq * D, Hkv * D)) return rc;
+  if (B < 1 || int64_t(B) * Hq * ((int64_t(max_seqlen_q) + 63) / 64) > kMaxBlocks) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k))
+    return FA_ERR_ALIGN;
+  const fa::FwdBf16Problem p{q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, D, total_q,
+                             total_k, max_seqlen_q, scale, causal != 0,
+                             static_cast<hipStream_t>(stream)};
+  return fa::launch_fwd_bf16_general(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int T, int D) {

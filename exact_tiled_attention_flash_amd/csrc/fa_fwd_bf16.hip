@@ -171,11 +171,28 @@ struct Sched {
 };
 static_assert(Sched<128>::valid() && Sched<64>::valid(), "pipeline schedule order");
 
+// Kernel arguments (element strides; the layouts are described with FwdBf16Problem).
+struct FwdKArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const int* cu_q;   // null: dense
+  const int* cu_k;
+  int64_t q_bs, q_hs, kv_bs, kv_hs, lse_bs, lse_hs;   // batch and head strides
+  int q_rs, kv_rs;   // row strides of q / o and of k / v
+  int Tq, Tk;        // dense lengths, or total rows of the packed arrays
+  int G;             // query heads per K/V head
+  int HG;            // head groups per batch (Hq / heads per workgroup)
+  int hpw_log2;      // log2 of the query heads per workgroup (1, 2 or 4 heads)
+  int nbhg;          // B * HG
+  int nq;            // query tiles per (batch, head group)
+  float c;           // scale * log2(e)
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int T, int BH, int nq, float c) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs args) {
   using Tl = SwzTile<D>;
   using S = Sched<D>;
   constexpr int nD = D / 32;   // 32-row blocks of O^T
@@ -194,17 +211,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
+  const float c = args.c;
+  // Workgroup -> (query tile, batch, head group): heaviest causal tiles first, (batch, head
+  // group) fastest. A workgroup serves hpw query heads that share one K/V head, each with
+  // 256 / hpw consecutive queries (64 per wave), so every K/V tile it loads feeds all of them.
   const int L = workgroup_id();
-  const int bh = L % BH;
-  int qt = L / BH;
-  if (CAUSAL) qt = nq - 1 - qt;
-  const int q0 = qt * kBlockM;
-  const int qw0 = q0 + wave * 64;
+  const int r = L % args.nbhg;
+  int qt = L / args.nbhg;
+  if (CAUSAL) qt = args.nq - 1 - qt;
+  const int b = r / args.HG, hg = r % args.HG;
+  const int hpw = 1 << args.hpw_log2;
+  const int h0 = hg * hpw;
+  const int hq = h0 + (wave & (hpw - 1));             // this wave's query head
+  const int kvh = h0 / args.G;                            // the workgroup's K/V head
+  const int qrows = kBlockM >> args.hpw_log2;             // queries per head in this workgroup
+  // sequence bounds (packed batches: clamped into the arrays whatever the offsets hold)
+  int qs = 0, Tq = args.Tq, ks = 0, Tk = args.Tk;
+  if (args.cu_q) {
+    qs = min(max(args.cu_q[b], 0), args.Tq);
+    Tq = min(max(args.cu_q[b + 1], qs), args.Tq) - qs;
+    ks = min(max(args.cu_k[b], 0), args.Tk);
+    Tk = min(max(args.cu_k[b + 1], ks), args.Tk) - ks;
+    qs = __builtin_amdgcn_readfirstlane(qs);
+    Tq = __builtin_amdgcn_readfirstlane(Tq);
+    ks = __builtin_amdgcn_readfirstlane(ks);
+    Tk = __builtin_amdgcn_readfirstlane(Tk);
+  }
+  const int q0 = qt * qrows;
+  if (q0 >= Tq) return;   // past this sequence's queries (packed batches); uniform per workgroup
+  const int qw0 = q0 + (wave >> args.hpw_log2) * 64;
+  const int shift = CAUSAL ? Tk - Tq : 0;   // bottom-right alignment: 0 when Tq == Tk
 
-  const size_t base = (size_t)bh * T * D;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const uint16_t* Qh = args.q + b * args.q_bs + (int64_t)qs * args.q_rs + hq * args.q_hs;
+  uint16_t* Oh = args.o + b * args.q_bs + (int64_t)qs * args.q_rs + hq * args.q_hs;
+  float* Lh = args.lse + b * args.lse_bs + hq * args.lse_hs + qs;
+  const uint16_t* Kh = args.k + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
+  const uint16_t* Vh = args.v + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
+  const int T = Tk;   // key rows of this sequence (tile loads clamp to T - 1)
   auto kslot = [&](int t) -> uint8_t* { return (t & 1) ? ks1 : ks0; };
   auto vslot = [&](int t) -> uint8_t* { return (t & 1) ? vs1 : vs0; };
   // jp: parity of j as IC<0> / IC<1>, or IC<-1> when only known at run time
@@ -218,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if constexpr (P < 0) return vslot(j + d);
     else return ((P + d) & 1) ? vs1 : vs0;
   };
-  const TileLoader<D> ld(wave, lane);
+  const TileLoader<D> ld(wave, lane, args.kv_rs);
 
   // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
   // d = 16 kk + 8 h + 0..7.
@@ -228,8 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int qrow = qw0 + 32 * qb + l32;
 #pragma unroll
     for (int kk = 0; kk < nK; ++kk) {
-      u32x4 x = qrow < T ? *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + kk * 16 + h * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
+      u32x4 x = qrow < Tq
+                    ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
       qf[qb][kk] = as_bf16x8(x);
     }
   }
@@ -244,10 +288,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
 
-  const int kend = CAUSAL ? min(T, q0 + kBlockM) : T;
-  const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  // keys seen by the workgroup's last query, and by all of its queries
+  const int kend = CAUSAL ? min(Tk, q0 + qrows + shift) : Tk;
+  const int ntiles = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  const int kall = CAUSAL ? min(Tk, q0 + shift + 1) : Tk;
   // tiles [0, nfull) need no mask for any query of this workgroup
-  const int nfull = min((CAUSAL ? min(q0, T) : T) / kBlockN, ntiles);
+  const int nfull = kall > 0 ? min(kall / kBlockN, ntiles) : 0;
+
+  if (ntiles == 0) {   // no query of this workgroup sees a key (uniform per workgroup)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qrow = qw0 + 32 * qb + l32;
+      if (qrow < Tq) {
+        uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
+#pragma unroll
+        for (int d0 = 0; d0 < D; d0 += 8)
+          if ((d0 / 8) % 2 == h) *reinterpret_cast<u32x4*>(orow + d0) = u32x4{0u, 0u, 0u, 0u};
+        if (h == 0) Lh[qrow] = kNegInf;
+      }
+    }
+    return;
+  }
 
   f32x16 acc[2][nD];
 #pragma unroll
@@ -284,8 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int k0 = t * kBlockN;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      int l = T - k0;
-      if (CAUSAL) l = min(l, qw0 + 32 * qb + l32 - k0 + 1);
+      int l = Tk - k0;
+      if (CAUSAL) l = min(l, qw0 + 32 * qb + l32 + shift - k0 + 1);
       lim[qb] = l - 4 * h;
     }
   };
@@ -347,7 +408,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   auto reduce = [&](float (&m_old)[2]) {
     float a = fmaxf(pm[0][0], pm[0][1]), b = fmaxf(pm[1][0], pm[1][1]);
     halves_max2(a, b, h);
-    const bool need = (a - m_ref[0]) * c > kRescaleLog2 || (b - m_ref[1]) * c > kRescaleLog2;
+    // (a reference still at -inf belongs to a row that has not seen a key yet)
+    const bool need = (a - m_ref[0]) * c > kRescaleLog2 || (b - m_ref[1]) * c > kRescaleLog2 ||
+                      m_ref[0] == kNegInf || m_ref[1] == kNegInf;
     const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
     m_old[0] = m_ref[0];
     m_old[1] = m_ref[1];
@@ -360,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   auto rescale = [&](const float (&m_old)[2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float alpha = exp2_fast((m_old[qb] - m_ref[qb]) * c);
+      const float alpha = m_old[qb] == m_ref[qb] ? 1.f : exp2_fast((m_old[qb] - m_ref[qb]) * c);
 #pragma unroll
       for (int db = 0; db < nD; ++db) acc[qb][db] *= alpha;
 #pragma unroll
@@ -517,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     for (int u = 0; u < 32; ++u) max_item(Par<0>{}, u >> 4, (u >> 3) & 1, u & 7, masked, lim);
     float a = fmaxf(pm[0][0], pm[0][1]), b = fmaxf(pm[1][0], pm[1][1]);
     halves_max2(a, b, h);
-    // every row sees key 0, so both maxima are finite
+    // a row that sees no key of tile 0 keeps -inf here; its exponentials are all masked to 0
     m_ref[0] = a;
     m_ref[1] = b;
     mc[0] = a * c;
@@ -556,9 +619,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const float r_half = rp[qb][0] + rp[qb][1];
     const float l_tot = l_half + swap_halves(l_half);
     const float r_tot = r_half + swap_halves(r_half);
-    if (qrow < T) {
-      const float inv = 1.0f / r_tot;
-      uint16_t* orow = O + base + (size_t)qrow * D;
+    if (qrow < Tq) {
+      // a row that sees no key at all (causal, fewer keys than queries) gets O = 0, LSE = -inf
+      const float inv = r_tot > 0.f ? 1.0f / r_tot : 0.f;
+      uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
 #pragma unroll
       for (int db = 0; db < nD; ++db) {
 #pragma unroll
@@ -569,28 +633,61 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
           *reinterpret_cast<u32x2*>(orow + d0) = w;
         }
       }
-      if (h == 0) LSE[(size_t)bh * T + qrow] = (m_ref[qb] * c + log2_fast(l_tot)) * kLn2;
+      if (h == 0) Lh[qrow] = l_tot > 0.f ? (m_ref[qb] * c + log2_fast(l_tot)) * kLn2 : kNegInf;
     }
   }
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch(const FwdArgs& a) {
-  const int BH = a.B * a.H;
-  const int nq = (a.T + kBlockM - 1) / kBlockM;
-  const float c = a.scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.T,
-                     BH, nq, c);
+hipError_t launch(const FwdBf16Problem& p) {
+  FwdKArgs k;
+  k.q = static_cast<const uint16_t*>(p.q);
+  k.k = static_cast<const uint16_t*>(p.k);
+  k.v = static_cast<const uint16_t*>(p.v);
+  k.o = static_cast<uint16_t*>(p.o);
+  k.lse = p.lse;
+  k.cu_q = p.cu_q;
+  k.cu_k = p.cu_k;
+  k.G = p.Hq / p.Hkv;
+  k.hpw_log2 = k.G % 4 == 0 ? 2 : (k.G % 2 == 0 ? 1 : 0);
+  k.HG = p.Hq >> k.hpw_log2;
+  k.nbhg = p.B * k.HG;
+  k.nq = (p.max_q + (kBlockM >> k.hpw_log2) - 1) / (kBlockM >> k.hpw_log2);
+  k.Tq = p.Tq;
+  k.Tk = p.Tk;
+  if (p.cu_q) {   // packed (rows, heads, D)
+    k.q_rs = p.Hq * D;
+    k.kv_rs = p.Hkv * D;
+    k.q_bs = k.kv_bs = 0;
+    k.q_hs = D;
+    k.kv_hs = D;
+    k.lse_bs = 0;
+    k.lse_hs = p.Tq;
+  } else {        // (B, heads, rows, D)
+    k.q_rs = k.kv_rs = D;
+    k.q_hs = (int64_t)p.Tq * D;
+    k.kv_hs = (int64_t)p.Tk * D;
+    k.q_bs = (int64_t)p.Hq * k.q_hs;
+    k.kv_bs = (int64_t)p.Hkv * k.kv_hs;
+    k.lse_hs = p.Tq;
+    k.lse_bs = (int64_t)p.Hq * p.Tq;
+  }
+  k.c = p.scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_fwd_bf16_general(const FwdBf16Problem& p) {
+  if (p.D == 64) return p.causal ? launch<64, true>(p) : launch<64, false>(p);
+  return p.causal ? launch<128, true>(p) : launch<128, false>(p);
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.D == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  const FwdBf16Problem p{a.q, a.k, a.v, a.o, a.lse, nullptr, nullptr, a.B, a.H, a.H, a.D,
+                         a.T, a.T, a.T, a.scale, a.causal, a.stream};
+  return launch_fwd_bf16_general(p);
 }
 
 }  // namespace fa

@@ -28,7 +28,27 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// General bf16 forward: grouped K/V heads (Hq = G * Hkv), queries and keys of different
+// lengths, and packed variable-length batches. Dense: q, o are (B, Hq, Tq, D), k, v are
+// (B, Hkv, Tk, D), lse is (B, Hq, Tq). Packed (cu_q, cu_k non-null, B + 1 entries each): q, o
+// are (Tq, Hq, D) and k, v are (Tk, Hkv, D) with Tq, Tk the total rows, sequence b owning rows
+// [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]); lse is (Hq, Tq). Causal is aligned at the
+// bottom right: query i of a sequence sees key j iff j <= i + (Tk_b - Tq_b).
+struct FwdBf16Problem {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int *cu_q, *cu_k;
+  int B, Hq, Hkv, D;
+  int Tq, Tk;    // dense: lengths; packed: total rows
+  int max_q;     // longest query sequence (dense: Tq)
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs &a);
+hipError_t launch_fwd_bf16_general(const FwdBf16Problem &p);
 hipError_t launch_fwd_f32(const FwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a);
 

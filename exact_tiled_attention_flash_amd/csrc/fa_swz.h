@@ -40,14 +40,18 @@ struct SwzTile {
 // the logical chunk the swizzle maps there. The lane's rows and in-row byte offsets do not
 // depend on the tile and are computed once; per load only the row clamp and one multiply-add
 // remain. Rows at or beyond T are clamped to row T - 1; callers mask or never store
-// whatever depends on them. `wave` must be wave-uniform (it selects the LDS destination).
+// whatever depends on them. `wave` must be wave-uniform (it selects the LDS destination); rows
+// of the source are `row_stride` elements apart (D for a (rows x D) matrix, H*D for one head
+// of a packed (rows, H, D) array), and rows up to T of one source stay below 2^31 bytes.
 template <int D>
 struct TileLoader {
   using Tl = SwzTile<D>;
   int row[Tl::loadsPerWave];        // tile row of the lane's i-th chunk
   uint32_t cofs[Tl::loadsPerWave];  // byte offset of that chunk within its row
   int wave;
-  __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
+  uint32_t rsb;                     // bytes between consecutive rows of the source matrix
+  __device__ __forceinline__ TileLoader(int wave_, int lane, int row_stride = D)
+      : wave(wave_), rsb((uint32_t)row_stride * 2u) {
 #pragma unroll
     for (int i = 0; i < Tl::loadsPerWave; ++i) {
       const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
@@ -59,7 +63,7 @@ struct TileLoader {
   __device__ __forceinline__ void issue(uint8_t* dst, const uint16_t* __restrict__ src, int row0,
                                         int T, int i) const {
     // 32-bit byte offset from the wave-uniform base (one head is below 2^31 bytes)
-    const uint32_t off = (uint32_t)min(row0 + row[i], T - 1) * (uint32_t)(D * 2) + cofs[i];
+    const uint32_t off = (uint32_t)min(row0 + row[i], T - 1) * rsb + cofs[i];
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + off,
                                      (lds_void*)(dst + (wave * Tl::loadsPerWave + i) * 1024), 16,
                                      0, 0);

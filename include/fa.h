@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 enum fa_dtype {
     FA_F32 = 0,
@@ -90,6 +90,50 @@ const char *fa_status_string(int status);
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int T, int D, float scale, int causal, int dtype,
            void *stream);
+
+/*
+ * Forward with grouped K/V heads and separate query and key lengths (FA_BF16 only).
+ *   q      in:  (B, Hq, Tq, D) bf16
+ *   k, v   in:  (B, Hkv, Tk, D) bf16; Hq must be a multiple G of Hkv and query
+ *               head h attends with K/V head h / G
+ *   o      out: (B, Hq, Tq, D) bf16
+ *   lse    out: (B, Hq, Tq) float32
+ * Causal masking is aligned at the bottom right: query i sees key j iff
+ * j <= i + (Tk - Tq) (the top-left rule of fa_fwd when Tq == Tk). A query that
+ * sees no key (possible when Tk < Tq) gets o = 0 and lse = -inf.
+ * One workgroup serves up to four query heads of a group, so every K/V tile it
+ * loads feeds all of them. Tq, Tk >= 1; the rows of one head of any tensor stay
+ * below 2^31 bytes (FA_ERR_SHAPE otherwise).
+ * Source: "Lab 06 - Attention kernels", "Check yourself" question 7 and its
+ * answer (GQA: map the program to a K/V head so a tile loaded once serves the
+ * query heads sharing it), and the build-order table, step 2 (query and key
+ * lengths may differ).
+ */
+int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale,
+               int causal, int dtype, void *stream);
+
+/*
+ * Forward over a packed batch of B variable-length sequences (FA_BF16 only).
+ *   cu_seqlens_q, cu_seqlens_k  in: device int32 arrays of B + 1 offsets (4-byte
+ *               aligned): sequence b owns query rows [cu_seqlens_q[b],
+ *               cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b],
+ *               cu_seqlens_k[b+1]). The kernels clamp the offsets into
+ *               [0, total] and treat a decreasing pair as an empty sequence, so
+ *               no access leaves the arrays whatever they hold.
+ *   q      in:  (total_q, Hq, D) bf16;  k, v in: (total_k, Hkv, D) bf16
+ *   o      out: (total_q, Hq, D) bf16;  lse out: (Hq, total_q) float32
+ *   max_seqlen_q  bound on every query length (sizes the grid; rows of a
+ *               longer sequence beyond it are left unwritten)
+ * Heads and masking as fa_fwd_gqa, per sequence. Rows not covered by any
+ * sequence are left unwritten.
+ * Source: "Triton FlashAttention-2 forward", "Exercises" (a cu_seqlens index
+ * tensor packs requests of different lengths into one launch).
+ */
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq,
+                  int Hkv, int total_q, int total_k, int max_seqlen_q, int D,
+                  float scale, int causal, int dtype, void *stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: 8*B*H*T (the

@@ -5,7 +5,10 @@ this package. The product (the HIP library and its binding) never does.
 """
 from .attention import (  # noqa: F401
     attention_backward,
+    attention_cross,
     attention_forward,
+    attention_forward_gqa,
+    attention_forward_varlen,
     attention_forward_online,
     attention_rows,
     backward_delta,

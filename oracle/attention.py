@@ -205,3 +205,80 @@ def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool):
 def backward_delta(o, do):
     """D_i = sum_d dO_id * O_id ([Lab06] section 4 and "Check yourself" answer 6)."""
     return np.sum(o * do, axis=-1)
+
+
+def attention_cross(q_h, k_h, v_h, scale: float, causal: bool):
+    """One head with Tq query rows against Tk key rows: (O, LSE) in float64.
+
+    [Lab06] the build-order table, step 2: query and key lengths may differ.
+    The pages fix no causal rule for Tq != Tk; the reading taken is the
+    bottom-right one: query i sees key j iff j <= i + (Tk - Tq), which is the
+    top-left rule of `scores` when Tq == Tk. A row that sees no key at all
+    (only possible when Tk < Tq) gets O = 0 and LSE = -inf. S is materialised
+    in chunks of query rows, softmax in two passes.
+    """
+    Tq, Tk = q_h.shape[0], k_h.shape[0]
+    o = np.zeros((Tq, v_h.shape[1]), dtype=np.float64)
+    lse = np.full(Tq, -np.inf)
+    keys = np.arange(Tk)
+    for r0 in range(0, Tq, _ROW_CHUNK):
+        rows = np.arange(r0, min(Tq, r0 + _ROW_CHUNK))
+        s = (q_h[rows] @ k_h.T) * scale
+        if causal:
+            s = np.where(keys[None, :] <= rows[:, None] + (Tk - Tq), s, -np.inf)
+        seen = np.isfinite(s).any(axis=1)
+        if seen.any():
+            _, _, row_lse = softmax_stats(s[seen])
+            p = np.exp(s[seen] - row_lse[:, None])
+            o[rows[seen]] = p @ v_h
+            lse[rows[seen]] = row_lse
+    return o, lse
+
+
+def attention_forward_gqa(q, k, v, scale: float, causal: bool):
+    """Grouped K/V heads: q (B, Hq, Tq, D), k and v (B, Hkv, Tk, D), Hq = G * Hkv.
+
+    [Lab06] "Check yourself" question 7 and its answer: the query heads of a
+    group share one K/V head; query head h uses K/V head h // G. Every (b, h)
+    is `attention_cross` on its own K/V head. Returns O (B, Hq, Tq, D) and
+    LSE (B, Hq, Tq).
+    """
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype != np.float64 or x.ndim != 4:
+            raise ValueError(f"{name} must be a float64 (B, H, T, D) array")
+    B, Hq, Tq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != v.shape or Hq % Hkv or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"bad grouped shapes {q.shape} {k.shape} {v.shape}")
+    G = Hq // Hkv
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, Tq))
+    for b in range(B):
+        for h in range(Hq):
+            o[b, h], lse[b, h] = attention_cross(q[b, h], k[b, h // G], v[b, h // G], scale, causal)
+    return o, lse
+
+
+def attention_forward_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
+    """A packed batch: q (total_q, Hq, D), k and v (total_k, Hkv, D).
+
+    [FA2nb] "Exercises": a cu_seqlens index tensor packs requests of different
+    lengths into one launch. Sequence b owns query rows [cu_q[b], cu_q[b+1])
+    and key rows [cu_k[b], cu_k[b+1]); each sequence is grouped attention on
+    its own rows (`attention_cross` per head). Returns O (total_q, Hq, D),
+    zero on rows no sequence covers, and LSE (Hq, total_q), -inf there.
+    """
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    o = np.zeros_like(q)
+    lse = np.full((Hq, total_q), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 <= q0:
+            continue
+        for h in range(Hq):
+            ob, lb = attention_cross(q[q0:q1, h], k[k0:k1, h // G], v[k0:k1, h // G], scale, causal)
+            o[q0:q1, h] = ob
+            lse[h, q0:q1] = lb
+    return o, lse

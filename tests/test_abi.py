@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -121,3 +121,39 @@ def test_bwd_validation(lib):
     assert bwd(lib, scale=-1.0) == -6
     assert bwd(lib, causal=5) == -7
     assert bwd(lib, ws_bytes=127) == -7  # needs 8*B*H*T = 128 bytes
+
+
+def gqa(lib, Hq=4, Hkv=2, Tq=16, Tk=16, D=64, dtype=1, causal=0, scale=0.125, nulls=()):
+    ptrs = [None if i in nulls else P for i in range(5)]
+    return lib.fa_fwd_gqa(*ptrs, 1, Hq, Hkv, Tq, Tk, D, ctypes.c_float(scale), causal, dtype, None)
+
+
+def test_gqa_validation(lib):
+    for i in range(5):
+        assert gqa(lib, nulls=(i,)) == -1
+    assert gqa(lib, Hq=3, Hkv=2) == -2          # Hq not a multiple of Hkv
+    assert gqa(lib, Tq=0) == -2 and gqa(lib, Tk=0) == -2
+    assert gqa(lib, Tk=1 << 23, D=128) == -2    # one K head reaches 2^31 bytes
+    assert gqa(lib, D=96) == -3
+    assert gqa(lib, dtype=0) == -4              # bf16 only
+    assert gqa(lib, causal=3) == -7
+    assert gqa(lib, scale=float("nan")) == -6
+
+
+def varlen(lib, B=2, Hq=4, Hkv=2, tq=32, tk=32, maxq=16, D=64, dtype=1, cu=P, nulls=()):
+    ptrs = [None if i in nulls else P for i in range(5)]
+    cq = None if 5 in nulls else cu
+    ck = None if 6 in nulls else cu
+    return lib.fa_fwd_varlen(*ptrs, cq, ck, B, Hq, Hkv, tq, tk, maxq, D, ctypes.c_float(0.1), 1,
+                             dtype, None)
+
+
+def test_varlen_validation(lib):
+    for i in range(7):
+        assert varlen(lib, nulls=(i,)) == -1
+    assert varlen(lib, maxq=0) == -2 and varlen(lib, maxq=33) == -2   # 1 <= max <= total
+    assert varlen(lib, B=0) == -2
+    assert varlen(lib, tq=1 << 22, Hq=4, D=128, maxq=16) == -2          # (rows, heads, D) >= 2^31 B
+    assert varlen(lib, D=32) == -3
+    assert varlen(lib, dtype=0) == -4
+    assert varlen(lib, cu=P + 2) == -5                                  # offsets 4-byte aligned

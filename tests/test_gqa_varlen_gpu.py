@@ -1,0 +1,132 @@
+"""Grouped K/V heads, query / key lengths that differ, and packed variable-length batches on
+the GPU (fa_fwd_gqa, fa_fwd_varlen through the C ABI) against the CPU float64 oracle.
+
+Tolerances as for the forward: bf16 O max-abs <= 2e-2, LSE <= 1e-3. Causal masking with
+Tq != Tk is aligned at the bottom right (query i sees key j iff j <= i + Tk - Tq); rows that
+see no key must come back as O = 0, LSE = -inf exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL, as_f64, device_tensor, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_tiled_attention_flash_amd as m
+    return m
+
+
+def _bf16(shape, seed):
+    a = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    return synth.f32_to_bf16_bits(a)
+
+
+def _check(o, lse, o_ref, lse_ref, what):
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin), f"{what}: -inf rows differ"
+    assert np.all(lse[~fin] == -np.inf) and np.all(o[~fin] == 0), f"{what}: unseen rows"
+    err_o = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    err_l = float(np.max(np.abs(lse[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    assert err_o <= TOL["bf16"]["o"], f"{what} O max-abs {err_o:.3e}"
+    assert err_l <= TOL["bf16"]["lse"], f"{what} LSE max-abs {err_l:.3e}"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G,Tq,Tk", [(1, 100, 100), (2, 65, 65), (4, 200, 200), (8, 64, 64),
+                                     (4, 37, 300), (2, 130, 257), (4, 300, 45), (8, 1, 129),
+                                     (3, 70, 70)])
+def test_gqa_vs_oracle(fa, G, Tq, Tk, causal, D):
+    print(f"case gqa G={G} Tq={Tq} Tk={Tk} D={D} causal={causal}", flush=True)
+    B, Hkv = 2, 2
+    qb, kb, vb = _bf16((B, Hkv * G, Tq, D), 1), _bf16((B, Hkv, Tk, D), 2), _bf16((B, Hkv, Tk, D), 3)
+    scale = 1 / math.sqrt(D)
+    o, lse = fa.fa_fwd_gqa(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                           device_tensor(vb, "bf16"), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward_gqa(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                as_f64(vb, "bf16"), scale, causal)
+    _check(host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, f"G={G} Tq={Tq} Tk={Tk}")
+
+
+def test_gqa_single_group_equals_fa_fwd(fa):
+    # one query head per K/V head and Tq == Tk: the same kernel path as fa_fwd, bit for bit
+    d = synth.make_inputs(2, 4, 333, 128, "bf16", seed=5)
+    q, k, v = (device_tensor(d[n], "bf16") for n in "qkv")
+    for causal in (False, True):
+        o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
+        o2, l2 = fa.fa_fwd_gqa(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _pack(lens, H, D, seed):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return _bf16((int(cu[-1]), H, D), seed), cu
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [1, 4])
+def test_varlen_vs_oracle(fa, G, causal, D):
+    print(f"case varlen G={G} D={D} causal={causal}", flush=True)
+    lq = [1, 200, 0, 64, 513, 33, 7]
+    lk = [5, 200, 9, 64, 513, 100, 3]
+    Hkv = 2
+    qb, cq = _pack(lq, Hkv * G, D, 4)
+    kb, ck = _pack(lk, Hkv, D, 5)
+    vb, _ = _pack(lk, Hkv, D, 6)
+    scale = 1 / math.sqrt(D)
+    cu_q, cu_k = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    o, lse = fa.fa_fwd_varlen(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                              device_tensor(vb, "bf16"), cu_q, cu_k, max(lq), causal=causal,
+                              scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward_varlen(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                   as_f64(vb, "bf16"), cq, ck, scale, causal)
+    # LSE is (Hq, total_q); its transpose lines up with O's (total_q, Hq) rows
+    _check(host_f64(o), lse.cpu().numpy().astype(np.float64).T, o_ref, l_ref.T, "varlen")
+
+
+def test_varlen_equals_dense_when_lengths_match(fa):
+    # a packed batch of equal lengths is the dense call on the same data, bit for bit
+    B, H, T, D = 3, 4, 150, 128
+    d = synth.make_inputs(B, H, T, D, "bf16", seed=8)
+    q, k, v = (device_tensor(d[n], "bf16") for n in "qkv")
+    pack = lambda t: t.permute(0, 2, 1, 3).reshape(B * T, H, D).contiguous()
+    cu = torch.arange(0, (B + 1) * T, T, dtype=torch.int32, device="cuda")
+    for causal in (False, True):
+        o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
+        o2, l2 = fa.fa_fwd_varlen(pack(q), pack(k), pack(v), cu, cu, T, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(pack(o1), o2)
+        assert torch.equal(l1.permute(1, 0, 2).reshape(H, B * T), l2)
+
+
+def test_varlen_out_of_range_offsets_stay_in_bounds(fa):
+    # offsets past the arrays are clamped on the device: the call completes and the
+    # well-formed sequences are still exact
+    H, D = 2, 64
+    qb, cq = _pack([40, 40], H, D, 9)
+    kb, ck = _pack([40, 40], H, D, 10)
+    vb, _ = _pack([40, 40], H, D, 11)
+    bad_q = np.array([0, 40, 10_000_000], dtype=np.int32)
+    bad_k = np.array([0, 40, 99_999], dtype=np.int32)
+    o, lse = fa.fa_fwd_varlen(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                              device_tensor(vb, "bf16"), torch.from_numpy(bad_q).cuda(),
+                              torch.from_numpy(bad_k).cuda(), 40, causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward_varlen(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                   as_f64(vb, "bf16"), cq, ck, 0.125, True)
+    _check(host_f64(o)[:40], lse.cpu().numpy()[:, :40].astype(np.float64).T, o_ref[:40],
+           l_ref[:, :40].T, "first sequence")

@@ -372,3 +372,107 @@ def test_planted_backward_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(oattn, "attention_backward", real_bwd)
     monkeypatch.setattr(oracle, "attention_backward", real_bwd)
     assert not ok
+
+
+# ---- grouped K/V heads, query / key lengths that differ, packed batches -----------------------
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_with_one_query_head_per_group_is_attention_forward(causal):
+    q, k, v = (_rand((2, 3, 37, 8), s) for s in (1, 2, 3))
+    o1, l1 = oracle.attention_forward_gqa(q, k, v, 0.3, causal)
+    o2, l2 = oracle.attention_forward(q, k, v, 0.3, causal)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+def _bottom_right_mask(Tq, Tk):
+    i = torch.arange(Tq)[:, None]
+    j = torch.arange(Tk)[None, :]
+    return j <= i + (Tk - Tq)
+
+
+@pytest.mark.parametrize("G,Tq,Tk,causal", [(4, 23, 23, True), (2, 9, 31, True), (8, 17, 40, False),
+                                             (4, 12, 50, True), (1, 30, 7, False)])
+def test_gqa_matches_torch_sdpa_float64(G, Tq, Tk, causal):
+    # pinned to torch's float64 CPU attention with grouped heads and an explicit mask
+    B, Hkv, D = 2, 2, 16
+    q = _rand((B, Hkv * G, Tq, D), 4)
+    k, v = _rand((B, Hkv, Tk, D), 5), _rand((B, Hkv, Tk, D), 6)
+    o, lse = oracle.attention_forward_gqa(q, k, v, 0.25, causal)
+    mask = _bottom_right_mask(Tq, Tk) if causal else None
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         attn_mask=mask, scale=0.25, enable_gqa=True).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    # LSE against scipy on scores built with each query head's own K/V head
+    kk = np.repeat(k, G, axis=1)
+    s = np.einsum("bhqd,bhkd->bhqk", q, kk) * 0.25
+    if causal:
+        s = np.where(_bottom_right_mask(Tq, Tk).numpy(), s, -np.inf)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_cross_causal_uniform_scores_closed_form():
+    # q = 0: every visible key has score 0, so O_i = mean(V[0 : i + Tk - Tq + 1]) and
+    # LSE_i = ln(i + Tk - Tq + 1); with Tk < Tq the first Tq - Tk rows see nothing.
+    Tk, D = 6, 3
+    v = _rand((Tk, D), 7)
+    for Tq in (4, 6, 9):
+        o, lse = oracle.attention_cross(np.zeros((Tq, D)), _rand((Tk, D), 8), v, 0.7, True)
+        for i in range(Tq):
+            n = i + Tk - Tq + 1
+            if n <= 0:
+                assert np.all(o[i] == 0) and lse[i] == -np.inf
+            else:
+                np.testing.assert_allclose(o[i], v[:n].mean(axis=0), rtol=0, atol=1e-14)
+                assert abs(lse[i] - math.log(n)) < 1e-14
+
+
+def test_varlen_is_attention_per_sequence():
+    Hq, Hkv, D = 4, 2, 8
+    lq, lk = [5, 0, 17, 1, 33], [7, 3, 17, 12, 20]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = _rand((cu_q[-1], Hq, D), 9)
+    k, v = _rand((cu_k[-1], Hkv, D), 10), _rand((cu_k[-1], Hkv, D), 11)
+    for causal in (False, True):
+        o, lse = oracle.attention_forward_varlen(q, k, v, cu_q, cu_k, 0.4, causal)
+        for b in range(len(lq)):
+            if lq[b] == 0:
+                continue
+            sl_q, sl_k = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+            qs = torch.from_numpy(np.ascontiguousarray(q[sl_q].transpose(1, 0, 2)))[None]
+            ks = torch.from_numpy(np.ascontiguousarray(k[sl_k].transpose(1, 0, 2)))[None]
+            vs = torch.from_numpy(np.ascontiguousarray(v[sl_k].transpose(1, 0, 2)))[None]
+            mask = _bottom_right_mask(lq[b], lk[b]) if causal else None
+            seen = mask.any(dim=1).numpy() if causal else np.ones(lq[b], bool)
+            ref = F.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask, scale=0.4,
+                                                 enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+            np.testing.assert_allclose(o[sl_q][seen], ref[seen], rtol=0, atol=1e-12)
+            assert np.all(o[sl_q][~seen] == 0) and np.all(lse[:, sl_q][:, ~seen] == -np.inf)
+
+
+def test_planted_gqa_mistakes_are_caught(monkeypatch):
+    # a top-left causal rule, or query head h using K/V head h % Hkv, must fail the pins
+    q = _rand((1, 4, 9, 8), 12)
+    k, v = _rand((1, 2, 14, 8), 13), _rand((1, 2, 14, 8), 14)
+    mask = _bottom_right_mask(9, 14)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                         attn_mask=mask, scale=0.3, enable_gqa=True).numpy()
+
+    def top_left(q_h, k_h, v_h, scale, causal):
+        s = (q_h @ k_h.T) * scale
+        s = np.where(np.arange(k_h.shape[0])[None] <= np.arange(q_h.shape[0])[:, None], s, -np.inf)
+        _, _, lse = oattn.softmax_stats(s)
+        return np.exp(s - lse[:, None]) @ v_h, lse
+    monkeypatch.setattr(oattn, "attention_cross", top_left)
+    o_bad, _ = oattn.attention_forward_gqa(q, k, v, 0.3, True)
+    assert np.abs(o_bad - ref).max() > 1e-3
+    monkeypatch.undo()
+    o_ok, _ = oattn.attention_forward_gqa(q, k, v, 0.3, True)
+    np.testing.assert_allclose(o_ok, ref, rtol=0, atol=1e-12)
+    o_mod = np.stack([oattn.attention_cross(q[0, h], k[0, h % 2], v[0, h % 2], 0.3, True)[0]
+                      for h in range(4)])[None]
+    assert np.abs(o_mod - ref).max() > 1e-3
