@@ -7,7 +7,10 @@ workload: causal bf16, B=4, H=16, T=4096, D=128, scale 1/sqrt(128), seeded
 N(0,1) inputs already resident in HBM. FLOPs per step = 4*B*H*T^2*D / 2.
 The backward (fa_bwd, three kernels) is measured the same way on its own
 workload (causal bf16, B=2, H=16, T=4096, D=128) and reported under
-"backward". The CPU baseline times the float64 oracle on a bounded sample of
+"backward". The further rows of the forward are timed on their own workloads
+and reported under "next_rows": grouped K/V heads (B=4, 32 query heads over 8
+K/V heads, T=4096, causal) and a packed batch of 32 causal sequences of 64 to
+8192 tokens (16 heads). The CPU baseline times the float64 oracle on a bounded sample of
 the forward workload (whole (b, h) heads) on the host cores.
 Prints one JSON line.
 """
@@ -101,6 +104,52 @@ def cpu_baseline(w, d, budget_s: float):
                       f"{el:.1f} s", "seconds": el}
 
 
+def next_rows(torch, fa, metrics, steps, warmup):
+    """Time the grouped-head and packed variable-length forwards; one launch per step."""
+    import synth
+    peak = metrics.PEAK_TFLOPS["bf16"]
+    rows = {}
+
+    w = synth.GQA_WORKLOADS["gqa_bf16_b4hq32hkv8t4096d128_causal"]
+    d = synth.make_gqa_inputs(w, seed=0)
+    q, k, v = (_dev(d[n], torch) for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
+    total, per, _ = _time_launches(
+        torch, lambda: fa.fa_fwd_gqa(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
+        steps, warmup)
+    flops = metrics.gqa_flops(w.B, w.Hq, w.Tq, w.Tk, w.D, w.causal)
+    ms = total / steps
+    rows["gqa"] = {"workload": w.name, "ms_per_step": round(ms, 5),
+                   "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                   "pct_of_bf16_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / peak, 2),
+                   "flops_per_step": flops,
+                   "algorithmic_bytes_per_step": metrics.gqa_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk,
+                                                                   w.D, 2)}
+    del q, k, v, o, lse
+
+    w = synth.VARLEN_WORKLOADS["varlen_bf16_n32l64to8192h16d128_causal"]
+    d = synth.make_varlen_inputs(w, seed=0)
+    q, k, v = (_dev(d[n], torch) for n in "qkv")
+    cu = torch.from_numpy(d["cu"]).to("cuda")
+    maxlen = int(d["lens"].max())
+    o = torch.empty_like(q)
+    lse = torch.empty((w.Hq, q.shape[0]), dtype=torch.float32, device="cuda")
+    total, per, _ = _time_launches(
+        torch, lambda: fa.fa_fwd_varlen(q, k, v, cu, cu, maxlen, causal=w.causal, scale=w.scale,
+                                        out=o, lse=lse), steps, warmup)
+    flops = metrics.varlen_flops(d["lens"], d["lens"], w.Hq, w.D, w.causal)
+    ms = total / steps
+    rows["varlen"] = {"workload": w.name, "total_tokens": int(d["cu"][-1]), "max_len": maxlen,
+                      "ms_per_step": round(ms, 5),
+                      "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                      "pct_of_bf16_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / peak, 2),
+                      "flops_per_step": flops,
+                      "algorithmic_bytes_per_step": metrics.varlen_bytes(
+                          q.shape[0], k.shape[0], w.Hq, w.Hkv, w.D, 2)}
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +157,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (counter calibration under rocprofv3)")
@@ -200,6 +250,9 @@ def main():
                            "flops_per_step": bflops,
                            "flop_count": "10*B*H*T^2*D/2 (S recompute, dP, dV, dQ, dK)",
                            "pct_of_bf16_peak": round(100.0 * bflops / (bms * 1e-3) / 1e12 / peak, 2)}
+
+    if not args.no_next_rows:
+        out["next_rows"] = next_rows(torch, fa, metrics, max(5, args.steps // 2), args.warmup)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d, args.cpu_budget)

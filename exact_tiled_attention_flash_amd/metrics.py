@@ -38,3 +38,24 @@ def bwd_bytes(B: int, H: int, T: int, D: int, elem_bytes: int) -> int:
 def score_matrix_bytes(B: int, H: int, T: int, elem_bytes: int) -> int:
     """Bytes of the T x T score matrix a naive implementation would write."""
     return elem_bytes * B * H * T * T
+
+
+def gqa_flops(B: int, Hq: int, Tq: int, Tk: int, D: int, causal: bool) -> float:
+    """Two Tq x Tk x D products per query head; a causal mask halves the count (the
+    convention above, exact in the limit Tq = Tk)."""
+    f = 4.0 * B * Hq * Tq * Tk * D
+    return f / 2.0 if causal else f
+
+
+def gqa_bytes(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, D: int, elem_bytes: int) -> int:
+    """Q read and O written per query head, K and V read once per K/V head, fp32 LSE."""
+    return elem_bytes * B * D * (2 * Hq * Tq + 2 * Hkv * Tk) + 4 * B * Hq * Tq
+
+
+def varlen_flops(lens_q, lens_k, Hq: int, D: int, causal: bool) -> float:
+    """Sum of the per-sequence forward counts."""
+    return sum(gqa_flops(1, Hq, int(a), int(b), D, causal) for a, b in zip(lens_q, lens_k))
+
+
+def varlen_bytes(total_q: int, total_k: int, Hq: int, Hkv: int, D: int, elem_bytes: int) -> int:
+    return elem_bytes * D * (2 * Hq * total_q + 2 * Hkv * total_k) + 4 * Hq * total_q

@@ -76,6 +76,7 @@ def attention_rows(q_bh, k_bh, v_bh, scale: float, causal: bool, rows: np.ndarra
     and section 3 (O and LSE are what the tiled method returns).
     """
     rows = np.asarray(rows, dtype=np.int64)
+    k_bh, v_bh = np.ascontiguousarray(k_bh), np.ascontiguousarray(v_bh)
     s = scores(q_bh, k_bh, scale, causal, rows)
     _, _, lse = softmax_stats(s)
     p = np.exp(s - lse[:, None])
@@ -217,6 +218,9 @@ def attention_cross(q_h, k_h, v_h, scale: float, causal: bool):
     (only possible when Tk < Tq) gets O = 0 and LSE = -inf. S is materialised
     in chunks of query rows, softmax in two passes.
     """
+    # head slices of packed (rows, H, D) arrays are strided; numpy's products on them are
+    # an order of magnitude slower than on a contiguous copy (same values)
+    q_h, k_h, v_h = (np.ascontiguousarray(x) for x in (q_h, k_h, v_h))
     Tq, Tk = q_h.shape[0], k_h.shape[0]
     o = np.zeros((Tq, v_h.shape[1]), dtype=np.float64)
     lse = np.full(Tq, -np.inf)

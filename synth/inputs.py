@@ -119,3 +119,86 @@ def make_inputs(B: int, H: int, T: int, D: int, dtype: str = "bf16", seed: int =
 def make_workload_inputs(w: Workload, seed: int = 0) -> dict:
     return make_inputs(w.B, w.H, w.T, w.D, w.dtype, seed=seed, with_do=w.backward,
                        spike_frac=w.spike_frac, spike_scale=w.spike_scale)
+
+
+@dataclasses.dataclass(frozen=True)
+class GqaWorkload:
+    """Grouped K/V heads: Q (B, Hq, Tq, D), K and V (B, Hkv, Tk, D), Hkv dividing Hq."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    Tk: int
+    D: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of n_seq sequences whose lengths are drawn log-uniformly from
+    [min_len, max_len]; Q (total, Hq, D), K and V (total, Hkv, D), the same lengths for
+    queries and keys (self-attention)."""
+
+    name: str
+    n_seq: int
+    min_len: int
+    max_len: int
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+
+GQA_WORKLOADS = {
+    w.name: w
+    for w in [
+        # 32 query heads sharing 8 K/V heads, headline length
+        GqaWorkload("gqa_bf16_b4hq32hkv8t4096d128_causal", 4, 32, 8, 4096, 4096, 128, True),
+    ]
+}
+
+VARLEN_WORKLOADS = {
+    w.name: w
+    for w in [
+        # 32 sequences of 64 .. 8192 tokens, 16 heads
+        VarlenWorkload("varlen_bf16_n32l64to8192h16d128_causal", 32, 64, 8192, 16, 16, 128, True),
+    ]
+}
+
+
+def make_gqa_inputs(w: GqaWorkload, seed: int = 0) -> dict:
+    """bf16 bits of Q (B, Hq, Tq, D), then K and V (B, Hkv, Tk, D), drawn in that order."""
+    rng = np.random.default_rng(seed)
+    out = {"q": rng.standard_normal((w.B, w.Hq, w.Tq, w.D), dtype=np.float32)}
+    for name in ("k", "v"):
+        out[name] = rng.standard_normal((w.B, w.Hkv, w.Tk, w.D), dtype=np.float32)
+    return {n: f32_to_bf16_bits(a) for n, a in out.items()}
+
+
+def varlen_lengths(rng: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:
+    """n lengths, log-uniform on [lo, hi], rounded to integers."""
+    x = np.exp(rng.uniform(math.log(lo), math.log(hi), n))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+def make_varlen_inputs(w: VarlenWorkload, seed: int = 0) -> dict:
+    """Lengths first, then bf16 bits of packed Q, K, V; cu_seqlens int32 (n_seq + 1)."""
+    rng = np.random.default_rng(seed)
+    lens = varlen_lengths(rng, w.n_seq, w.min_len, w.max_len)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    out = {"lens": lens, "cu": cu,
+           "q": f32_to_bf16_bits(rng.standard_normal((total, w.Hq, w.D), dtype=np.float32))}
+    for name in ("k", "v"):
+        out[name] = f32_to_bf16_bits(rng.standard_normal((total, w.Hkv, w.D), dtype=np.float32))
+    return out
