@@ -6,13 +6,17 @@ this package. The product (the HIP library and its binding) never does.
 from .attention import (  # noqa: F401
     attention_backward,
     attention_cross,
+    attention_decode,
     attention_forward,
     attention_forward_gqa,
     attention_forward_varlen,
     attention_forward_online,
     attention_rows,
+    attention_split_k,
     backward_delta,
+    merge_partials,
     online_softmax_stats,
     scores,
     softmax_stats,
+    split_partial,
 )

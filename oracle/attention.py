@@ -286,3 +286,85 @@ def attention_forward_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
             o[q0:q1, h] = ob
             lse[h, q0:q1] = lb
     return o, lse
+
+
+def attention_decode(q, k, v, cache_seqlens, scale: float, causal: bool):
+    """New query rows against a K/V cache: q (B, Hq, Tq, D), k and v (B, Hkv, Tk, D).
+
+    [Lab06] "Check yourself" question 2 and the "Stretch" list (decoding against
+    a long K/V cache). Sequence b attends to its first cache_seqlens[b] keys
+    (all Tk when cache_seqlens is None; counts clamped into [0, Tk]); the
+    result is the definition, `attention_cross` on those keys with the grouped
+    head mapping of `attention_forward_gqa` (bottom-right causal alignment, so
+    the last query row sees every valid key). Returns O (B, Hq, Tq, D) and
+    LSE (B, Hq, Tq).
+    """
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros_like(q)
+    lse = np.full((B, Hq, Tq), -np.inf)
+    for b in range(B):
+        L = Tk if cache_seqlens is None else int(min(max(int(cache_seqlens[b]), 0), Tk))
+        if L == 0:
+            continue
+        for h in range(Hq):
+            o[b, h], lse[b, h] = attention_cross(q[b, h], k[b, h // G, :L], v[b, h // G, :L],
+                                                 scale, causal)
+    return o, lse
+
+
+def split_partial(q_h, k_h, v_h, scale: float, key_lo: int, key_hi: int, limits):
+    """Partial softmax state of query rows over the keys [key_lo, key_hi).
+
+    [Lab06] "Check yourself" answer 2: each program of a split-K decode keeps
+    its own (m, l, acc) over its share of the keys. `limits[i]` is the last key
+    row i may see (masking); keys outside the range or beyond the limit do not
+    count. A row that sees no key of the range has m = -inf, l = 0, acc = 0
+    (the guard the page's "Common bugs" list asks for when key ranges are
+    visited out of order). Returns (m, l, acc) in the natural-log domain.
+    """
+    q_h, k_h, v_h = (np.ascontiguousarray(x) for x in (q_h, k_h, v_h))
+    Tq = q_h.shape[0]
+    keys = np.arange(key_lo, key_hi)
+    s = (q_h @ k_h[key_lo:key_hi].T) * scale
+    s = np.where(keys[None, :] <= np.asarray(limits)[:, None], s, -np.inf)
+    m = np.max(s, axis=1) if key_hi > key_lo else np.full(Tq, -np.inf)
+    safe = np.where(np.isneginf(m), 0.0, m)
+    p = np.exp(s - safe[:, None])
+    return m, np.sum(p, axis=1), p @ v_h[key_lo:key_hi]
+
+
+def merge_partials(ms, ls, accs):
+    """Merge split-K partial states: [Lab06] "Check yourself" answer 2 (the same
+    rescaling rule as the online recurrence). With m* = max_s m_s, every partial
+    is weighted by exp(m_s - m*) (0 for an empty partial); O = sum w acc / sum w l
+    and LSE = m* + ln(sum w l). Rows with no key in any partial: O = 0,
+    LSE = -inf. Inputs are lists over splits of (rows,), (rows,), (rows, D).
+    """
+    ms, ls, accs = np.stack(ms), np.stack(ls), np.stack(accs)
+    m_star = np.max(ms, axis=0)
+    seen = ~np.isneginf(m_star)
+    safe = np.where(seen, m_star, 0.0)
+    w = np.where(np.isneginf(ms), 0.0, np.exp(ms - safe[None, :]))
+    l = np.sum(w * ls, axis=0)
+    acc = np.sum(w[:, :, None] * accs, axis=0)
+    o = np.zeros(acc.shape)
+    o[seen] = acc[seen] / l[seen, None]
+    lse = np.full(m_star.shape, -np.inf)
+    lse[seen] = m_star[seen] + np.log(l[seen])
+    return o, lse
+
+
+def attention_split_k(q_h, k_h, v_h, scale: float, causal: bool, bounds):
+    """One head by split-K: partial states over the key ranges [bounds[s],
+    bounds[s+1]) ([Lab06] "Stretch": FlashDecoding), merged by `merge_partials`.
+    Same masking convention as `attention_cross` (bottom-right causal). Exists to
+    show that split-and-merge reaches the definition, including empty ranges and
+    ranges a row cannot see.
+    """
+    Tq, Tk = q_h.shape[0], k_h.shape[0]
+    limits = np.arange(Tq) + (Tk - Tq) if causal else np.full(Tq, Tk - 1)
+    parts = [split_partial(q_h, k_h, v_h, scale, int(bounds[s]), int(bounds[s + 1]), limits)
+             for s in range(len(bounds) - 1)]
+    return merge_partials(*zip(*parts))

@@ -476,3 +476,124 @@ def test_planted_gqa_mistakes_are_caught(monkeypatch):
     o_mod = np.stack([oattn.attention_cross(q[0, h], k[0, h % 2], v[0, h % 2], 0.3, True)[0]
                       for h in range(4)])[None]
     assert np.abs(o_mod - ref).max() > 1e-3
+
+
+# ---------------------------------------------------------------- split-K decode
+SPLIT_CASES = [(1, 50, False), (1, 50, True), (4, 37, True), (6, 4, True), (3, 20, False)]
+
+
+def _split_pins(cases=SPLIT_CASES, trials=6):
+    """Split-and-merge over random key ranges (empty ones included) against the definition."""
+    rng = np.random.default_rng(20)
+    for Tq, Tk, causal in cases:
+        q, k, v = _rand((Tq, 8), 21), _rand((Tk, 8), 22), _rand((Tk, 8), 23)
+        o_ref, l_ref = oracle.attention_cross(q, k, v, 0.45, causal)
+        seen = np.isfinite(l_ref)
+        for _ in range(trials):
+            cuts = np.sort(rng.integers(0, Tk + 1, rng.integers(0, 6)))
+            bounds = np.concatenate([[0], cuts, [Tk]])
+            o, lse = oracle.attention_split_k(q, k, v, 0.45, causal, bounds)
+            if not (np.array_equal(np.isfinite(lse), seen) and np.all(np.isfinite(o))
+                    and np.max(np.abs(o - o_ref)) <= 1e-13
+                    and np.max(np.abs(lse[seen] - l_ref[seen]), initial=0.0) <= 1e-13
+                    and np.all(o[~seen] == 0)):
+                return False
+    return True
+
+
+def test_split_k_reaches_the_definition():
+    # [Lab06] "Check yourself" answer 2: partial (m, l, acc) per key range, merged with the
+    # rescaling rule, equals exact attention; ranges a row cannot see (causal) and empty ranges
+    # contribute nothing, and a row that sees no key at all ends as O = 0, LSE = -inf
+    assert _split_pins()
+
+
+def test_split_k_single_range_is_the_partial_normalised():
+    q, k, v = _rand((3, 8), 24), _rand((11, 8), 25), _rand((11, 8), 26)
+    m, l, acc = oracle.split_partial(q, k, v, 0.5, 0, 11, np.full(3, 10))
+    s = (q @ k.T) * 0.5
+    np.testing.assert_allclose(m, s.max(axis=1), rtol=0, atol=0)
+    np.testing.assert_allclose(m + np.log(l), scipy.special.logsumexp(s, axis=1), rtol=0, atol=1e-13)
+    o, lse = oracle.merge_partials([m], [l], [acc])
+    np.testing.assert_allclose(o, scipy.special.softmax(s, axis=1) @ v, rtol=0, atol=1e-13)
+
+
+def test_planted_merge_mistakes_are_caught(monkeypatch):
+    # each plausible slip in the merge fails the split pins
+    real = oattn.merge_partials
+
+    def no_weights(ms, ls, accs):
+        ms, ls, accs = np.stack(ms), np.stack(ls), np.stack(accs)
+        m = np.max(ms, axis=0)
+        return np.sum(accs, 0) / np.sum(ls, 0)[:, None], m + np.log(np.sum(ls, 0))
+
+    def no_empty_guard(ms, ls, accs):
+        ms, ls, accs = np.stack(ms), np.stack(ls), np.stack(accs)
+        m = np.max(ms, axis=0)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            w = np.exp(ms - m[None, :])
+            l = np.sum(w * ls, 0)
+            return np.sum(w[:, :, None] * accs, 0) / l[:, None], m + np.log(l)
+
+    def unweighted_lse(ms, ls, accs):
+        o, lse = real(ms, ls, accs)
+        m = np.max(np.stack(ms), axis=0)
+        with np.errstate(divide="ignore"):
+            return o, m + np.log(np.sum(np.stack(ls), 0))
+
+    for wrong in (no_weights, no_empty_guard, unweighted_lse):
+        monkeypatch.setattr(oattn, "merge_partials", wrong)
+        with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
+            assert not _split_pins(), wrong.__name__
+    monkeypatch.setattr(oattn, "merge_partials", real)
+    assert _split_pins()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_matches_torch_sdpa_float64(causal):
+    # pinned to torch's float64 CPU attention on each sequence's valid keys, LSE to torch's
+    # logsumexp of the explicit scores
+    B, Hq, Hkv, Tq, Tk, D = 4, 8, 2, 3, 40, 16
+    q, k, v = _rand((B, Hq, Tq, D), 30), _rand((B, Hkv, Tk, D), 31), _rand((B, Hkv, Tk, D), 32)
+    lens = [40, 17, 2, 0]
+    o, lse = oracle.attention_decode(q, k, v, lens, 0.3, causal)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(o[b] == 0) and np.all(lse[b] == -np.inf)
+            continue
+        mask = _bottom_right_mask(Tq, L) if causal else torch.ones(Tq, L, dtype=torch.bool)
+        seen = mask.any(dim=1).numpy()
+        qt = torch.from_numpy(q[b:b + 1])
+        kt, vt = (torch.from_numpy(np.ascontiguousarray(x[b:b + 1, :, :L])) for x in (k, v))
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.3,
+                                             enable_gqa=True)[0].numpy()
+        s = torch.matmul(qt, kt.repeat_interleave(G, dim=1).transpose(-1, -2)) * 0.3
+        ref_lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)[0].numpy()
+        np.testing.assert_allclose(o[b][:, seen], ref[:, seen], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b][:, seen], ref_lse[:, seen], rtol=0, atol=1e-12)
+        assert np.all(o[b][:, ~seen] == 0) and np.all(lse[b][:, ~seen] == -np.inf)
+
+
+def test_decode_closed_forms():
+    # Q = 0 and one query row: O is the mean of the valid V rows, LSE = ln L; counts are
+    # clamped into [0, Tk]
+    B, Hq, Hkv, Tk, D = 4, 4, 4, 30, 8
+    v = _rand((B, Hkv, Tk, D), 33)
+    lens = [30, 99, 5, -3]
+    o, lse = oracle.attention_decode(np.zeros((B, Hq, 1, D)), _rand((B, Hkv, Tk, D), 34), v,
+                                     lens, 0.9, True)
+    for b, L in enumerate([30, 30, 5, 0]):
+        if L == 0:
+            assert np.all(o[b] == 0) and np.all(lse[b] == -np.inf)
+            continue
+        np.testing.assert_allclose(o[b, :, 0], v[b, :, :L].mean(axis=1), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[b, :, 0], math.log(L), rtol=0, atol=1e-14)
+
+
+def test_decode_without_lengths_is_gqa_forward():
+    q, k, v = _rand((2, 6, 2, 8), 35), _rand((2, 3, 25, 8), 36), _rand((2, 3, 25, 8), 37)
+    for causal in (False, True):
+        o1, l1 = oracle.attention_decode(q, k, v, None, 0.35, causal)
+        o2, l2 = oracle.attention_forward_gqa(q, k, v, 0.35, causal)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
