@@ -13,7 +13,9 @@ from ._lib import (  # noqa: F401
     fa_abi_version,
     fa_bwd,
     fa_bwd_workspace_bytes,
+    fa_decode_workspace_bytes,
     fa_fwd,
+    fa_fwd_decode,
     fa_fwd_gqa,
     fa_fwd_varlen,
     fa_status_string,

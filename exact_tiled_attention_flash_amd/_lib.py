@@ -50,6 +50,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_fwd_decode.restype = i
+    lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
     if hasattr(lib, "fa_bwd"):
         lib.fa_bwd.restype = i
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -186,6 +190,52 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q,
                            total_k, int(max_seqlen_q), D, float(scale), int(bool(causal)), FA_BF16,
                            _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, l
+
+
+def fa_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Tq: int, Tk: int, D: int,
+                              num_splits: int = 0) -> int:
+    return load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Tq, Tk, D, num_splits)
+
+
+def fa_fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  cache_seqlens: torch.Tensor | None = None, num_splits: int = 0,
+                  causal: bool = False, scale: float | None = None,
+                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None):
+    """Split-K decode against a K/V cache: q (B, Hq, Tq, D) with (Hq / Hkv) * Tq <= 32, k and v
+    (B, Hkv, Tk, D), bf16; cache_seqlens an int32 (B,) device tensor of valid keys per
+    sequence (None: all Tk). num_splits 0 picks the split count. Returns o (B, Hq, Tq, D) and
+    lse (B, Hq, Tq) float32. Enqueued on the current stream."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_plain(name, t, torch.bfloat16, 4)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be (B, Hkv, Tk, D) with q's B and D")
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if cache_seqlens is not None:
+        _check_plain("cache_seqlens", cache_seqlens, torch.int32, 1)
+        if cache_seqlens.numel() != B:
+            raise ValueError("cache_seqlens must hold B counts")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_plain("out", o, torch.bfloat16, 4)
+    _check_plain("lse", l, torch.float32, 3)
+    if o.shape != q.shape or tuple(l.shape) != (B, Hq, Tq):
+        raise ValueError("out must match q and lse must be (B, Hq, Tq)")
+    need = lib.fa_decode_workspace_bytes(B, Hq, Hkv, Tq, Tk, D, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = lib.fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                           None if cache_seqlens is None else cache_seqlens.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           B, Hq, Hkv, Tq, Tk, D, int(num_splits), float(scale),
+                           int(bool(causal)), FA_BF16, _stream(q))
     if rc != FA_OK:
         raise FaError(rc)
     return o, l

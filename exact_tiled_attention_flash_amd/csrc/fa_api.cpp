@@ -44,6 +44,29 @@ int check_sizes_general(int B, int Hq, int Hkv, int Tq, int Tk, int D, int q_rs,
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Query rows of one K/V head's group that one decode product holds.
+constexpr int kDecodeMaxRows = 32;
+constexpr int kDecodeKeys = 32;      // keys per decode tile
+constexpr int kDecodeTarget = 768;   // splits x (b, K/V head) aimed at: 3 per compute unit of 256
+
+// Split count of the decode: the caller's (clamped to the key tiles), or enough splits that
+// B * Hkv * splits is about kDecodeTarget.
+int decode_splits(int B, int Hkv, int Tk, int num_splits) {
+  const int nt = (Tk + kDecodeKeys - 1) / kDecodeKeys;
+  int64_t s = num_splits > 0 ? num_splits
+                             : (kDecodeTarget + int64_t(B) * Hkv - 1) / (int64_t(B) * Hkv);
+  if (s > nt) s = nt;
+  if (s > fa::decode_max_splits()) s = fa::decode_max_splits();
+  return s < 1 ? 1 : int(s);
+}
+
+int check_decode(int B, int Hq, int Hkv, int Tq, int Tk, int D, int num_splits) {
+  if (int rc = check_sizes_general(B, Hq, Hkv, Tq, Tk, D, D, D)) return rc;
+  if (int64_t(Hq / Hkv) * Tq > kDecodeMaxRows) return FA_ERR_SHAPE;
+  if (num_splits < 0) return FA_ERR_ARG;
+  return FA_OK;
+}
+
 int check_scale(float scale) {
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   return FA_OK;
@@ -118,6 +141,31 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                              total_k, max_seqlen_q, scale, causal != 0,
                              static_cast<hipStream_t>(stream)};
   return fa::launch_fwd_bf16_general(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, int num_splits) {
+  if (check_decode(B, Hq, Hkv, Tq, Tk, D, num_splits) != FA_OK) return 0;
+  const size_t s = decode_splits(B, Hkv, Tk, num_splits);
+  return sizeof(float) * size_t(B) * size_t(Hq) * size_t(Tq) * s * size_t(D + 4);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int* cache_seqlens, void* workspace, size_t workspace_bytes, int B, int Hq,
+                  int Hkv, int Tq, int Tk, int D, int num_splits, float scale, int causal, int dtype,
+                  void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  if (int rc = check_decode(B, Hq, Hkv, Tq, Tk, D, num_splits)) return rc;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  if (workspace_bytes < fa_decode_workspace_bytes(B, Hq, Hkv, Tq, Tk, D, num_splits)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace) || (cache_seqlens && !aligned4(cache_seqlens)))
+    return FA_ERR_ALIGN;
+  const fa::DecodeBf16Problem p{q, k, v, o, lse, cache_seqlens, workspace, B, Hq, Hkv, Tq, Tk, D,
+                                decode_splits(B, Hkv, Tk, num_splits), scale, causal != 0,
+                                static_cast<hipStream_t>(stream)};
+  return fa::launch_decode_bf16(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int T, int D) {

@@ -47,9 +47,27 @@ struct FwdBf16Problem {
   hipStream_t stream;
 };
 
+// Split-K decode: q, o (B, Hq, Tq, D) with G * Tq <= 32 (G = Hq / Hkv), k, v (B, Hkv, Tk, D),
+// lse (B, Hq, Tq); seqlens (B) or null gives the valid keys of each sequence (clamped into
+// [0, Tk]); workspace holds B * Hkv * nsplit * G * Tq * (D + 4) floats. Causal is aligned at
+// the bottom right of each sequence's valid keys.
+struct DecodeBf16Problem {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int *seqlens;
+  void *workspace;
+  int B, Hq, Hkv, Tq, Tk, D, nsplit;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs &a);
 hipError_t launch_fwd_bf16_general(const FwdBf16Problem &p);
 hipError_t launch_fwd_f32(const FwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a);
+hipError_t launch_decode_bf16(const DecodeBf16Problem &p);
+int decode_max_splits();
 
 }  // namespace fa

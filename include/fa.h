@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 enum fa_dtype {
     FA_F32 = 0,
@@ -133,6 +133,46 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                   const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq,
                   int Hkv, int total_q, int total_k, int max_seqlen_q, int D,
+                  float scale, int causal, int dtype, void *stream);
+
+/*
+ * Bytes of device workspace fa_fwd_decode needs for these sizes and this
+ * num_splits (0 = the automatic choice): 4 * B * Hq * Tq * splits * (D + 4),
+ * where splits is num_splits clamped to [1, min(ceil(Tk / 32), 1024)], or with
+ * num_splits = 0 the smallest count that gives about 768 (b, K/V head, split)
+ * workgroups, within the same bounds. Returns 0 if the sizes are invalid.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                                 int num_splits);
+
+/*
+ * Split-K decode: a few new query rows per sequence against a long K/V cache
+ * (FA_BF16 only). The same result as fa_fwd_gqa on the valid keys, computed
+ * with the keys of every (b, K/V head) split across workgroups.
+ *   q      in:  (B, Hq, Tq, D) bf16; (Hq / Hkv) * Tq must be <= 32
+ *   k, v   in:  (B, Hkv, Tk, D) bf16, the cache; query head h uses K/V head
+ *               h / (Hq / Hkv)
+ *   cache_seqlens in: NULL (every sequence has Tk valid keys) or a device int32
+ *               array of B counts (4-byte aligned); sequence b attends to keys
+ *               [0, cache_seqlens[b]), the count clamped into [0, Tk] on the
+ *               device
+ *   o      out: (B, Hq, Tq, D) bf16;  lse out: (B, Hq, Tq) float32
+ *   workspace   at least fa_decode_workspace_bytes(...) bytes owned by the
+ *               caller; partial results, contents on return unspecified
+ *   num_splits  key splits per (b, K/V head); 0 = automatic (see above)
+ * Causal masking is aligned at the bottom right of each sequence's valid keys
+ * L: query i sees key j iff j <= i + (L - Tq). A query that sees no key gets
+ * o = 0 and lse = -inf. Two kernels: the splits write their partial (max, sum,
+ * accumulator); the second merges them.
+ * Source: "Lab 06 - Attention kernels", "Check yourself" answer 2 (split-K:
+ * partition the keys, a partial (m, l, acc) per program, merge with the same
+ * rescaling rule), answer 7 (one program per K/V head serving the query heads
+ * that share it), and the "Stretch" list (FlashDecoding with a second merge
+ * kernel, measured at T_q = 1 against T_k = 32k).
+ */
+int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int *cache_seqlens, void *workspace, size_t workspace_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int D, int num_splits,
                   float scale, int causal, int dtype, void *stream);
 
 /*

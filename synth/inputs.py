@@ -167,6 +167,26 @@ GQA_WORKLOADS = {
     ]
 }
 
+# one new query row per head against a long K/V cache (split-K decode), and the same cache
+# read by a batch of 8 sequences whose valid lengths are drawn log-uniformly in [1024, 32768]
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        GqaWorkload("decode_bf16_b1hq32hkv8tk32768d128", 1, 32, 8, 1, 32768, 128, True),
+        GqaWorkload("decode_bf16_b8hq32hkv8tk32768d128_lens", 8, 32, 8, 1, 32768, 128, True),
+    ]
+}
+
+
+def decode_lengths(w: GqaWorkload, seed: int = 0) -> np.ndarray:
+    """Valid cache lengths of a decode batch: the full cache for one sequence, else drawn
+    log-uniformly in [Tk / 32, Tk] (a generator of its own, after the tensors' draws)."""
+    if w.B == 1:
+        return np.array([w.Tk], dtype=np.int32)
+    rng = np.random.default_rng(seed + 1)
+    return varlen_lengths(rng, w.B, max(1, w.Tk // 32), w.Tk).astype(np.int32)
+
+
 VARLEN_WORKLOADS = {
     w.name: w
     for w in [

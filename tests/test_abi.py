@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -157,3 +157,40 @@ def test_varlen_validation(lib):
     assert varlen(lib, D=32) == -3
     assert varlen(lib, dtype=0) == -4
     assert varlen(lib, cu=P + 2) == -5                                  # offsets 4-byte aligned
+
+
+def test_decode_workspace_bytes(lib):
+    # 4 * B * Hq * Tq * splits * (D + 4); automatic splits: ceil(768 / (B * Hkv)) within
+    # [1, min(ceil(Tk / 32), 1024)]
+    assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 32768, 128, 0) == 4 * 32 * 96 * 132
+    assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 32768, 128, 7) == 4 * 32 * 7 * 132
+    assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 100, 64, 0) == 4 * 32 * 4 * 68     # 4 tiles
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, 1, 1 << 20, 64, 5000) == 4 * 1024 * 68  # cap
+    assert lib.fa_decode_workspace_bytes(64, 8, 8, 1, 4096, 128, 0) == 4 * 64 * 8 * 2 * 132
+    assert lib.fa_decode_workspace_bytes(1, 64, 1, 1, 128, 128, 0) == 0   # 64 rows per group
+    assert lib.fa_decode_workspace_bytes(1, 8, 2, 9, 128, 128, 0) == 0    # 4 * 9 > 32
+    assert lib.fa_decode_workspace_bytes(1, 8, 2, 8, 128, 128, 0) > 0     # 4 * 8 = 32
+    assert lib.fa_decode_workspace_bytes(1, 8, 2, 1, 128, 128, -1) == 0
+
+
+def decode(lib, Hq=8, Hkv=2, Tq=1, Tk=64, D=128, ws=1 << 20, splits=0, dtype=1, causal=0,
+           scale=0.1, lens=P, nulls=()):
+    ptrs = [None if i in nulls else P for i in range(5)]
+    return lib.fa_fwd_decode(*ptrs, lens, None if 5 in nulls else P, ws, 2, Hq, Hkv, Tq, Tk, D,
+                             splits, ctypes.c_float(scale), causal, dtype, None)
+
+
+def test_decode_validation(lib):
+    for i in range(6):
+        assert decode(lib, nulls=(i,)) == -1
+    assert decode(lib, Hq=9) == -2                # Hq not a multiple of Hkv
+    assert decode(lib, Tq=9) == -2                # 4 * 9 query rows per group > 32
+    assert decode(lib, Tk=0) == -2
+    assert decode(lib, D=96) == -3
+    assert decode(lib, dtype=0) == -4
+    assert decode(lib, lens=P + 2) == -5          # lengths 4-byte aligned
+    assert decode(lib, scale=-1.0) == -6
+    assert decode(lib, causal=2) == -7
+    assert decode(lib, splits=-1) == -7
+    need = lib.fa_decode_workspace_bytes(2, 8, 2, 1, 64, 128, 0)
+    assert decode(lib, ws=need - 1) == -7
