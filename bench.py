@@ -10,7 +10,10 @@ workload (causal bf16, B=2, H=16, T=4096, D=128) and reported under
 "backward". The further rows of the forward are timed on their own workloads
 and reported under "next_rows": grouped K/V heads (B=4, 32 query heads over 8
 K/V heads, T=4096, causal) and a packed batch of 32 causal sequences of 64 to
-8192 tokens (16 heads). The CPU baseline times the float64 oracle on a bounded sample of
+8192 tokens (16 heads); the split-K decode of one query row against a 32768-key
+cache (batch 1, 32 query heads over 8 K/V heads; also a batch of 8 with valid
+lengths of 1k to 32k keys) in GB/s against the HBM peak, beside the forward
+kernel's time on the same cache. The CPU baseline times the float64 oracle on a bounded sample of
 the forward workload (whole (b, h) heads) on the host cores.
 Prints one JSON line.
 """
@@ -55,6 +58,23 @@ def _time_launches(torch, fn, steps, warmup):
     per = [a.elapsed_time(b) for a, b in ev]
     total = ev[0][0].elapsed_time(ev[-1][1])
     return total, per, wall_ms
+
+
+def _time_loop(torch, fn, steps, warmup):
+    """Warm up, then time `steps` back-to-back calls of fn() with one event pair around the
+    loop (for calls of tens of microseconds, where an event pair per call would leave gaps
+    of host time between the launches). Returns milliseconds per call."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 COPY_BYTES = 256 << 20
@@ -147,6 +167,36 @@ def next_rows(torch, fa, metrics, steps, warmup):
                       "flops_per_step": flops,
                       "algorithmic_bytes_per_step": metrics.varlen_bytes(
                           q.shape[0], k.shape[0], w.Hq, w.Hkv, w.D, 2)}
+    for name in ("decode_bf16_b1hq32hkv8tk32768d128", "decode_bf16_b8hq32hkv8tk32768d128_lens"):
+        w = synth.DECODE_WORKLOADS[name]
+        d = synth.make_gqa_inputs(w, seed=0)
+        q, k, v = (_dev(d[n], torch) for n in "qkv")
+        lens = synth.decode_lengths(w)
+        sl = torch.from_numpy(lens).to("cuda") if w.B > 1 else None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.fa_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.D),
+                         dtype=torch.uint8, device="cuda")
+        ms = _time_loop(
+            torch, lambda: fa.fa_fwd_decode(q, k, v, cache_seqlens=sl, causal=w.causal,
+                                            scale=w.scale, out=o, lse=lse, workspace=ws),
+            4 * steps, warmup)
+        nbytes = metrics.decode_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.D, int(lens.sum()), 2)
+        row = {"workload": w.name, "ms_per_step": round(ms, 5),
+               "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "pct_of_hbm_peak": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / metrics.PEAK_HBM_GBS, 2),
+               "algorithmic_bytes_per_step": nbytes,
+               "kernels": "split kernel + merge kernel, one step each"}
+        if w.B == 1:
+            # the forward kernel on the same cache with one query row, as the pages ask
+            fo = torch.empty_like(q)
+            fl = torch.empty_like(lse)
+            ftot, _, _ = _time_launches(
+                torch, lambda: fa.fa_fwd_gqa(q, k, v, causal=w.causal, scale=w.scale, out=fo,
+                                             lse=fl), max(3, steps // 4), 2)
+            row["forward_kernel_ms_per_step"] = round(ftot / max(3, steps // 4), 5)
+        rows["decode" if w.B == 1 else "decode_lens"] = row
+        del q, k, v, o, lse, ws
     return rows
 
 

@@ -47,7 +47,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Query rows of one K/V head's group that one decode product holds.
 constexpr int kDecodeMaxRows = 32;
 constexpr int kDecodeKeys = 32;      // keys per decode tile
-constexpr int kDecodeTarget = 768;   // splits x (b, K/V head) aimed at: 3 per compute unit of 256
+constexpr int kDecodeTarget = 1024;  // splits x (b, K/V head) aimed at: 4 per compute unit of 256
 
 // Split count of the decode: the caller's (clamped to the key tiles), or enough splits that
 // B * Hkv * splits is about kDecodeTarget.

@@ -328,7 +328,10 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(const DecKArgs a) {
   }
 }
 
-// ---- merge: one wave per output row -----------------------------------------------------
+// ---- merge: one workgroup per output row -------------------------------------------------
+// 256 threads: thread t reads columns 4 (t % (D / 4)) .. +3 of every (256 / (D / 4))-th split,
+// so the splits of a row are read in parallel with 16-byte loads; the split weights and the
+// per-group sums meet in LDS.
 struct MergeKArgs {
   const float* part;
   uint16_t* o;
@@ -336,35 +339,42 @@ struct MergeKArgs {
   int Hq, Hkv, G, Tq, M, nsplit, nwork, rows;   // rows = B * Hq * Tq
 };
 
-constexpr int kMergeWaves = 4;
+constexpr int kMergeThreads = 256;
 constexpr int kMaxSplit = 1024;
 
 template <int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const MergeKArgs a) {
-  __shared__ float wsh[kMergeWaves][kMaxSplit];
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const MergeKArgs a) {
+  constexpr int C4 = D / 4;                  // float4 columns of a row
+  constexpr int NG = kMergeThreads / C4;     // splits read in parallel
+  __shared__ float wsh[kMaxSplit];
+  __shared__ float red[3][kMergeThreads / 64];
+  __shared__ f32x4 part_o[NG][C4];
   const int tid = lane_thread_id();
-  const int wave = wave_id();
-  const int lane = tid & 63;
-  const int R = workgroup_id() * kMergeWaves + wave;
-  if (R >= a.rows) return;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int R = workgroup_id();
   const int qi = R % a.Tq;
   const int hq = (R / a.Tq) % a.Hq;
   const int b = R / (a.Tq * a.Hq);
   const int kvh = hq / a.G, g = hq % a.G;
-  const int r = g * a.Tq + qi;                         // row within the K/V head's group
-  const int64_t w0 = ((int64_t)b * a.Hkv + kvh) * a.nsplit;   // first split's work index
+  const int r = g * a.Tq + qi;                                   // row within the K/V group
+  const int64_t w0 = ((int64_t)b * a.Hkv + kvh) * a.nsplit;     // first split's work index
   const float* St = a.part + (int64_t)a.nwork * a.M * D;
 
+  // global max of the splits' m (exp2 domain)
   float mx = kNegInf;
-  for (int s = lane; s < a.nsplit; s += 64) mx = fmaxf(mx, St[((w0 + s) * a.M + r) * 4]);
+  for (int s = tid; s < a.nsplit; s += kMergeThreads) mx = fmaxf(mx, St[((w0 + s) * a.M + r) * 4]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  // every split empty (no visible key): weights 0, O = 0, LSE = -inf
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  // weights; a split that saw no key (m = -inf) weighs 0, and so does every split of a row
+  // that saw none (then O = 0, LSE = -inf)
   float sl = 0.f, slr = 0.f;
-  for (int s = lane; s < a.nsplit; s += 64) {
+  for (int s = tid; s < a.nsplit; s += kMergeThreads) {
     const f32x4 st = *reinterpret_cast<const f32x4*>(St + ((w0 + s) * a.M + r) * 4);
     const float w = st[0] == kNegInf ? 0.f : exp2_fast(st[0] - mx);
-    wsh[wave][s] = w;
+    wsh[s] = w;
     sl += w * st[1];
     slr += w * st[2];
   }
@@ -373,37 +383,42 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(const Me
     sl += __shfl_xor(sl, o, 64);
     slr += __shfl_xor(slr, o, 64);
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  constexpr int E = D / 64;   // elements of the row per lane
-  float o[E];
+  __syncthreads();   // wsh complete; red[0] read by everyone
+  if (lane == 0) {
+    red[1][wave] = sl;
+    red[2][wave] = slr;
+  }
+  const int c4 = tid % C4, sg = tid / C4;
+  const float* A = a.part + (w0 * a.M + r) * D + c4 * 4;
+  const int64_t stride = (int64_t)a.M * D;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int s = sg;
+  for (; s + 3 * NG < a.nsplit; s += 4 * NG) {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(A + s * stride);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(A + (s + NG) * stride);
+    const f32x4 x2 = *reinterpret_cast<const f32x4*>(A + (s + 2 * NG) * stride);
+    const f32x4 x3 = *reinterpret_cast<const f32x4*>(A + (s + 3 * NG) * stride);
+    acc += wsh[s] * x0 + wsh[s + NG] * x1 + wsh[s + 2 * NG] * x2 + wsh[s + 3 * NG] * x3;
+  }
+  for (; s < a.nsplit; s += NG) acc += wsh[s] * *reinterpret_cast<const f32x4*>(A + s * stride);
+  part_o[sg][c4] = acc;
+  __syncthreads();
+  if (tid < C4) {
+    f32x4 o = part_o[0][tid];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  const float* A = a.part + (w0 * a.M + r) * D + lane * E;
-  const int64_t split_stride = (int64_t)a.M * D;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float w = wsh[wave][s];
-    if constexpr (E == 2) {
-      const f32x2 x = *reinterpret_cast<const f32x2*>(A + s * split_stride);
-      o[0] += w * x[0];
-      o[1] += w * x[1];
-    } else {
-      o[0] += w * A[s * split_stride];
+    for (int k = 1; k < NG; ++k) o += part_o[k][tid];
+    const float lr_tot = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+    const u32x2 w = {pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+    *reinterpret_cast<u32x2*>(a.o + (int64_t)R * D + tid * 4) = w;
+    if (tid == 0) {
+      const float l_tot = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+      a.lse[R] = l_tot > 0.f ? (mx + log2_fast(l_tot)) * kLn2 : kNegInf;
     }
   }
-  const float inv = slr > 0.f ? 1.f / slr : 0.f;
-  uint16_t* Or = a.o + (int64_t)R * D + lane * E;
-  if constexpr (E == 2) {
-    *reinterpret_cast<uint32_t*>(Or) = pack_bf16x2(o[0] * inv, o[1] * inv);
-  } else {
-    Or[0] = (uint16_t)(pack_bf16x2(o[0] * inv, 0.f) & 0xffffu);
-  }
-  if (lane == 0) a.lse[R] = sl > 0.f ? (mx + log2_fast(sl)) * kLn2 : kNegInf;
 }
 
-constexpr int kSlots = 3;
+constexpr int kSlots = 2;
 
 template <int D>
 hipError_t launch_decode_d(const DecodeBf16Problem& p) {
@@ -420,8 +435,7 @@ hipError_t launch_decode_d(const DecodeBf16Problem& p) {
   const int rows = p.B * p.Hq * p.Tq;
   MergeKArgs ma{static_cast<const float*>(p.workspace), static_cast<uint16_t*>(p.o), p.lse, p.Hq,
                 p.Hkv, G, p.Tq, M, p.nsplit, nwork, rows};
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((rows + kMergeWaves - 1) / kMergeWaves),
-                     dim3(64 * kMergeWaves), 0, p.stream, ma);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(rows), dim3(kMergeThreads), 0, p.stream, ma);
   return hipGetLastError();
 }
 

@@ -59,3 +59,9 @@ def varlen_flops(lens_q, lens_k, Hq: int, D: int, causal: bool) -> float:
 
 def varlen_bytes(total_q: int, total_k: int, Hq: int, Hkv: int, D: int, elem_bytes: int) -> int:
     return elem_bytes * D * (2 * Hq * total_q + 2 * Hkv * total_k) + 4 * Hq * total_q
+
+
+def decode_bytes(B: int, Hq: int, Hkv: int, Tq: int, D: int, valid_keys: int, elem_bytes: int) -> int:
+    """K and V rows read once per K/V head (valid_keys summed over the batch), Q read and O
+    written once, fp32 LSE. The split partials are not algorithmic traffic."""
+    return elem_bytes * D * (2 * Hkv * valid_keys + 2 * B * Hq * Tq) + 4 * B * Hq * Tq

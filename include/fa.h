@@ -139,7 +139,7 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  * Bytes of device workspace fa_fwd_decode needs for these sizes and this
  * num_splits (0 = the automatic choice): 4 * B * Hq * Tq * splits * (D + 4),
  * where splits is num_splits clamped to [1, min(ceil(Tk / 32), 1024)], or with
- * num_splits = 0 the smallest count that gives about 768 (b, K/V head, split)
+ * num_splits = 0 the smallest count that gives about 1024 (b, K/V head, split)
  * workgroups, within the same bounds. Returns 0 if the sizes are invalid.
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D,

@@ -160,9 +160,9 @@ def test_varlen_validation(lib):
 
 
 def test_decode_workspace_bytes(lib):
-    # 4 * B * Hq * Tq * splits * (D + 4); automatic splits: ceil(768 / (B * Hkv)) within
+    # 4 * B * Hq * Tq * splits * (D + 4); automatic splits: ceil(1024 / (B * Hkv)) within
     # [1, min(ceil(Tk / 32), 1024)]
-    assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 32768, 128, 0) == 4 * 32 * 96 * 132
+    assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 32768, 128, 0) == 4 * 32 * 128 * 132
     assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 32768, 128, 7) == 4 * 32 * 7 * 132
     assert lib.fa_decode_workspace_bytes(1, 32, 8, 1, 100, 64, 0) == 4 * 32 * 4 * 68     # 4 tiles
     assert lib.fa_decode_workspace_bytes(1, 1, 1, 1, 1 << 20, 64, 5000) == 4 * 1024 * 68  # cap
