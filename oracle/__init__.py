@@ -20,3 +20,4 @@ from .attention import (  # noqa: F401
     softmax_stats,
     split_partial,
 )
+from . import fp8  # noqa: F401,E402  (block-scaled E4M3 quantizer and the FP8 Q K^T reference)
