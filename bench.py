@@ -13,7 +13,9 @@ K/V heads, T=4096, causal) and a packed batch of 32 causal sequences of 64 to
 8192 tokens (16 heads); the split-K decode of one query row against a 32768-key
 cache (batch 1, 32 query heads over 8 K/V heads; also a batch of 8 with valid
 lengths of 1k to 32k keys) in GB/s against the HBM peak, beside the forward
-kernel's time on the same cache. The CPU baseline times the float64 oracle on a bounded sample of
+kernel's time on the same cache; and the forward with block-scaled E4M3 Q and K for Q K^T on
+the headline workload (TFLOP/s, with and without the quantization of Q and K, and its
+difference from the bf16 kernel's O and LSE). The CPU baseline times the float64 oracle on a bounded sample of
 the forward workload (whole (b, h) heads) on the host cores.
 Prints one JSON line.
 """
@@ -167,6 +169,39 @@ def next_rows(torch, fa, metrics, steps, warmup):
                       "flops_per_step": flops,
                       "algorithmic_bytes_per_step": metrics.varlen_bytes(
                           q.shape[0], k.shape[0], w.Hq, w.Hkv, w.D, 2)}
+    # FP8 (block-scaled E4M3) Q K^T on the headline workload: quantize Q and K, then the
+    # forward on the codes; accuracy as the difference from the bf16 kernel's result
+    w = synth.WORKLOADS["fwd_bf16_b4h16t4096d128_causal"]
+    d = synth.make_workload_inputs(w, seed=0)
+    q, k, v = (_dev(d[n], torch) for n in "qkv")
+    q8, qs = fa.fa_quantize_mxfp8(q)
+    k8, ks = fa.fa_quantize_mxfp8(k)
+    o8 = torch.empty_like(q)
+    l8 = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
+    total, _, _ = _time_launches(
+        torch, lambda: fa.fa_fwd_fp8qk(q8, qs, k8, ks, v, causal=True, scale=w.scale, out=o8, lse=l8),
+        steps, warmup)
+    ms = total / steps
+    qms = _time_loop(torch, lambda: (fa.fa_quantize_mxfp8(q, q8, qs), fa.fa_quantize_mxfp8(k, k8, ks)),
+                     steps, warmup)
+    flops = metrics.fwd_flops(w.B, w.H, w.T, w.D, True)
+    ob, lb = fa.fa_fwd(q, k, v, causal=True, scale=w.scale)
+    fa.fa_fwd_fp8qk(q8, qs, k8, ks, v, causal=True, scale=w.scale, out=o8, lse=l8)
+    torch.cuda.synchronize()
+    # S is half the flops at the fp8 rate (5.0 PFLOP/s), P V half at the bf16 rate
+    mixed_peak = 1.0 / (0.5 / 5000.0 + 0.5 / peak)
+    rows["fp8qk"] = {"workload": w.name, "ms_per_step": round(ms, 5),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "pct_of_bf16_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / peak, 2),
+                     "pct_of_mixed_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / mixed_peak, 2),
+                     "mixed_peak_tflops": round(mixed_peak, 1),
+                     "quantize_q_and_k_ms": round(qms, 5),
+                     "tflops_with_quantize": round(flops / ((ms + qms) * 1e-3) / 1e12, 2),
+                     "max_abs_o_vs_bf16_kernel": round((o8.float() - ob.float()).abs().max().item(), 5),
+                     "max_abs_lse_vs_bf16_kernel": round((l8 - lb).abs().max().item(), 5),
+                     "flops_per_step": flops}
+    del q, k, v, q8, k8, qs, ks, o8, l8, ob, lb
+
     for name in ("decode_bf16_b1hq32hkv8tk32768d128", "decode_bf16_b8hq32hkv8tk32768d128_lens"):
         w = synth.DECODE_WORKLOADS[name]
         d = synth.make_gqa_inputs(w, seed=0)

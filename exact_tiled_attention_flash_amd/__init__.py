@@ -16,8 +16,10 @@ from ._lib import (  # noqa: F401
     fa_decode_workspace_bytes,
     fa_fwd,
     fa_fwd_decode,
+    fa_fwd_fp8qk,
     fa_fwd_gqa,
     fa_fwd_varlen,
+    fa_quantize_mxfp8,
     fa_status_string,
     load_library,
 )

@@ -50,6 +50,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_quantize_mxfp8.restype = i
+    lib.fa_quantize_mxfp8.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.fa_fwd_fp8qk.restype = i
+    lib.fa_fwd_fp8qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_decode.restype = i
@@ -190,6 +194,62 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q,
                            total_k, int(max_seqlen_q), D, float(scale), int(bool(causal)), FA_BF16,
                            _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, l
+
+
+def fa_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None):
+    """Block-scaled E4M3 of a contiguous bf16 device tensor (..., D), D a multiple of 32: codes
+    uint8 (..., D) and scale bytes uint8 (..., D / 32). Enqueued on the current stream."""
+    lib = load_library()
+    if not x.is_cuda or not x.is_contiguous() or x.dtype != torch.bfloat16 or x.dim() < 1:
+        raise ValueError("x must be a contiguous bf16 device tensor")
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    c = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
+    s = (torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
+         if scales is None else scales)
+    _check_plain("codes", c, torch.uint8, x.dim())
+    _check_plain("scales", s, torch.uint8, x.dim())
+    if c.shape != x.shape or tuple(s.shape) != tuple(x.shape[:-1]) + (D // 32,):
+        raise ValueError("codes must match x and scales must be (..., D / 32)")
+    rc = lib.fa_quantize_mxfp8(x.data_ptr(), c.data_ptr(), s.data_ptr(), rows, D, FA_BF16, _stream(x))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return c, s
+
+
+def fa_fwd_fp8qk(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
+                 v: torch.Tensor, causal: bool = False, scale: float | None = None,
+                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Forward with E4M3 Q and K (codes and scales from fa_quantize_mxfp8): q8 (B, Hq, Tq, D),
+    k8 (B, Hkv, Tk, D) uint8, v (B, Hkv, Tk, D) bf16. Returns o (B, Hq, Tq, D) bf16 and lse
+    (B, Hq, Tq) float32. Enqueued on the current stream."""
+    lib = load_library()
+    _check_plain("q8", q8, torch.uint8, 4)
+    _check_plain("k8", k8, torch.uint8, 4)
+    _check_plain("v", v, torch.bfloat16, 4)
+    B, Hq, Tq, D = q8.shape
+    Hkv, Tk = k8.shape[1], k8.shape[2]
+    if v.shape != k8.shape or k8.shape[0] != B or k8.shape[3] != D:
+        raise ValueError("k8 and v must be (B, Hkv, Tk, D) with q8's B and D")
+    _check_plain("q_scale", q_scale, torch.uint8, 4)
+    _check_plain("k_scale", k_scale, torch.uint8, 4)
+    if tuple(q_scale.shape) != (B, Hq, Tq, D // 32) or tuple(k_scale.shape) != (B, Hkv, Tk, D // 32):
+        raise ValueError("scales must be (..., D / 32) of the codes' leading shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Hq, Tq, D), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check_plain("out", o, torch.bfloat16, 4)
+    _check_plain("lse", l, torch.float32, 3)
+    if tuple(o.shape) != (B, Hq, Tq, D) or tuple(l.shape) != (B, Hq, Tq):
+        raise ValueError("out must be (B, Hq, Tq, D) and lse (B, Hq, Tq)")
+    rc = lib.fa_fwd_fp8qk(q8.data_ptr(), q_scale.data_ptr(), k8.data_ptr(), k_scale.data_ptr(),
+                          v.data_ptr(), o.data_ptr(), l.data_ptr(), B, Hq, Hkv, Tq, Tk, D,
+                          float(scale), int(bool(causal)), _stream(q8))
     if rc != FA_OK:
         raise FaError(rc)
     return o, l

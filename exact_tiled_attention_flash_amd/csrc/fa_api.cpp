@@ -143,6 +143,38 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   return fa::launch_fwd_bf16_general(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_quantize_mxfp8(const void* x, void* codes, void* scales, int rows, int D, int dtype,
+                      void* stream) {
+  if (!x || !codes || !scales) return FA_ERR_NULL;
+  if (rows < 1 || D < 32 || D % 32 != 0) return FA_ERR_SHAPE;
+  if (int64_t(rows) * D > kMaxElems) return FA_ERR_SHAPE;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(scales)) return FA_ERR_ALIGN;
+  return fa::launch_quantize_mxfp8(x, codes, scales, int64_t(rows) * D,
+                                   static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FA_OK
+             : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8qk(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                 const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Tq, int Tk, int D,
+                 float scale, int causal, void* stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v || !o || !lse) return FA_ERR_NULL;
+  if (int rc = check_sizes_general(B, Hq, Hkv, Tq, Tk, D, D, D)) return rc;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned4(q_scale) || !aligned4(k_scale))
+    return FA_ERR_ALIGN;
+  fa::FwdBf16Problem p{q8, k8, v, o, lse, nullptr, nullptr, B, Hq, Hkv, D, Tq, Tk, Tq,
+                       scale, causal != 0, static_cast<hipStream_t>(stream)};
+  p.q8 = q8;
+  p.q_scale = q_scale;
+  p.k8 = k8;
+  p.k_scale = k_scale;
+  return fa::launch_fwd_bf16_general(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, int num_splits) {
   if (check_decode(B, Hq, Hkv, Tq, Tk, D, num_splits) != FA_OK) return 0;
   const size_t s = decode_splits(B, Hkv, Tk, num_splits);

@@ -66,6 +66,85 @@ __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void mfma_o(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
+// E4M3 variant of the S products: 32 x 32 x 64 with a power-of-two scale per 32 k-values.
+// Lane l supplies row (A) / column (B) l % 32; its bytes 0-15 are k-values 16 (l / 32) + 0..15
+// of the first 32-value block and bytes 16-31 the same positions of the second block; the
+// scale of block q of a row comes from lane row + 32 q, byte BYTE of its scale register
+// (op_sel carries bit 0 of BYTE, op_sel_hi bit 1).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <bool FIRST, int BYTE>
+__device__ __forceinline__ void mfma8_s(f32x16& d, const i32x8& a, const i32x8& b, uint32_t sa,
+                                        uint32_t sb) {
+  static_assert(BYTE == 0 || BYTE == 2, "scale byte");
+  if constexpr (FIRST && BYTE == 0)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4"
+                 : "=&v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+  else if constexpr (FIRST)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[1,1,0]"
+                 : "=&v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+  else if constexpr (BYTE == 0)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4"
+                 : "+v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+  else
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,1,0]"
+                 : "+v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+}
+
+// A [64 x D] E4M3 tile in LDS (D bytes a row, 16-byte chunks XOR-swizzled so that 8 (D = 128)
+// or 4 (D = 64) consecutive rows reading one logical chunk hit distinct banks for 32 and for
+// 64 banks), followed by its block-scale bytes: D / 32 per row, in one dword per row (a direct
+// HBM -> LDS load of 1 or 2 bytes a lane writes a zero-extended dword a lane).
+template <int D>
+struct SwzTile8 {
+  static constexpr int CH = D / 16;
+  static constexpr int RB = D;
+  static constexpr int SB = D / 32;     // scale bytes per row in HBM
+  static constexpr int sc_offset = 64 * RB;
+  static constexpr int loadsPerWave = 64 * CH / 256;
+  __device__ static __forceinline__ int swz(int row) { return D == 128 ? (row & 7) : ((row >> 1) & 3); }
+  __device__ static __forceinline__ int offset(int row, int lchunk) {
+    return row * RB + ((lchunk ^ swz(row)) << 4);
+  }
+};
+
+// Direct HBM -> LDS loads of a 64-row E4M3 tile and its scales by the 4 waves of a workgroup
+// (the same lane-to-chunk rule as TileLoader); wave 0 also moves the 64 rows' scale bytes.
+template <int D>
+struct TileLoader8 {
+  using Tl = SwzTile8<D>;
+  int row[Tl::loadsPerWave];
+  uint32_t cofs[Tl::loadsPerWave];
+  int wave, lane;
+  uint32_t rsb, srs;   // bytes between rows of the codes and of the scales
+  __device__ __forceinline__ TileLoader8(int wave_, int lane_, int row_stride)
+      : wave(wave_), lane(lane_), rsb((uint32_t)row_stride), srs((uint32_t)row_stride / 32u) {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) {
+      const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
+      row[i] = u / Tl::CH;
+      cofs[i] = (uint32_t)(((u % Tl::CH) ^ Tl::swz(row[i])) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(uint8_t* dst, const uint8_t* __restrict__ src, int row0,
+                                        int T, int i) const {
+    const uint32_t off = (uint32_t)min(row0 + row[i], T - 1) * rsb + cofs[i];
+    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(dst + (wave * Tl::loadsPerWave + i) * 1024),
+                                     16, 0, 0);
+  }
+  __device__ __forceinline__ void issue_scales(uint8_t* dst, const uint8_t* __restrict__ src,
+                                               int row0, int T) const {
+    if (wave == 0) {
+      const uint32_t off = (uint32_t)min(row0 + lane, T - 1) * srs;
+      __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(dst + Tl::sc_offset), Tl::SB, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue_all(uint8_t* dst, const uint8_t* __restrict__ src,
+                                            const uint8_t* __restrict__ ssrc, int row0, int T) const {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, src, row0, T, i);
+    issue_scales(dst, ssrc, row0, T);
+  }
+};
 // 20 wait states (more than the result latency of a 32x32x16 product) between the last
 // product writing x and y and any later instruction that uses them.
 __device__ __forceinline__ void fence2(f32x16& x, f32x16& y) {
@@ -189,9 +268,12 @@ struct FwdKArgs {
   int nbhg;          // B * HG
   int nq;            // query tiles per (batch, head group)
   float c;           // scale * log2(e)
+  // E4M3 Q K^T: codes of q / k (same layout and strides as q / k, one byte an element) and
+  // their block scales (one byte per 32 elements of a row: element offset / 32)
+  const uint8_t *q8, *k8, *qs, *ks;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool QK8>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs args) {
   using Tl = SwzTile<D>;
   using S = Sched<D>;
@@ -199,6 +281,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
   constexpr int nK = D / 16;   // k-steps of S^T
   constexpr int nKF = 2 * nK;  // K operand fragments per tile: f = nK kb + kk
   constexpr int nVF = 4 * nD;  // V operand fragments per tile: g = nD cc + db
+  using Tl8 = SwzTile8<D>;
+  constexpr int nK8 = D / 64;    // k-steps of an E4M3 S product
+  constexpr int nKF8 = 2 * nK8;  // E4M3 K fragments per tile: f = nK8 kb + kk
+  // odd steps of phase X that issue K loads (E4M3: the codes, then one for the scales)
+  constexpr int LK = QK8 ? Tl8::loadsPerWave + 1 : Tl::loadsPerWave;
   // Two slots per tensor, each its own LDS object: where the slot parity is known at compile
   // time the compiler can tell a slot being refilled by DMA from the one being read, and
   // need not wait for the DMA before every LDS read.
@@ -262,31 +349,79 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     else return ((P + d) & 1) ? vs1 : vs0;
   };
   const TileLoader<D> ld(wave, lane, args.kv_rs);
+  const TileLoader8<D> ld8(wave, lane, args.kv_rs);
+  const uint8_t *Kh8 = nullptr, *Ksh = nullptr;
+  if constexpr (QK8) {
+    const int64_t ko = b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
+    Kh8 = args.k8 + ko;
+    Ksh = args.ks + ko / 32;
+  }
 
   // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
-  // d = 16 kk + 8 h + 0..7.
-  bf16x8 qf[2][nK];
+  // d = 16 kk + 8 h + 0..7. E4M3: codes of k-step kk at d = 64 kk + 16 h + 0..15 and
+  // 64 kk + 32 + 16 h + 0..15, and the row's scale bytes shifted so that byte 2 kk is block
+  // 2 kk + h (the block whose scale this lane half supplies).
+  bf16x8 qf[2][QK8 ? 1 : nK];
+  i32x8 qf8[2][QK8 ? nK8 : 1];
+  uint32_t qsc[2] = {0u, 0u};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = qw0 + 32 * qb + l32;
+    if constexpr (!QK8) {
 #pragma unroll
-    for (int kk = 0; kk < nK; ++kk) {
-      u32x4 x = qrow < Tq
-                    ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-      qf[qb][kk] = as_bf16x8(x);
+      for (int kk = 0; kk < nK; ++kk) {
+        u32x4 x = qrow < Tq
+                      ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
+        qf[qb][kk] = as_bf16x8(x);
+      }
+    } else {
+      const int64_t qe = b * args.q_bs + (int64_t)(qs + qrow) * args.q_rs + hq * args.q_hs;
+      const uint8_t* Qr = args.q8 + qe;
+#pragma unroll
+      for (int kk = 0; kk < nK8; ++kk) {
+        u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+        if (qrow < Tq) {
+          x0 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 16 * h);
+          x1 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 32 + 16 * h);
+        }
+        qf8[qb][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+      uint32_t sc = 0x7f7f7f7fu;
+      if (qrow < Tq) {
+        const uint8_t* Qs = args.qs + qe / 32;
+        sc = D == 128 ? *reinterpret_cast<const uint32_t*>(Qs) : *reinterpret_cast<const uint16_t*>(Qs);
+      }
+      qsc[qb] = sc >> (8 * h);
     }
   }
   // Move Q^T into AGPRs now and pad the accumulator writes before any product reads them.
+  if constexpr (!QK8) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+      for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
+      for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kk = 0; kk < nK8; ++kk) asm volatile("" : "+a"(qf8[qb][kk]));
+      asm volatile("" : "+v"(qsc[qb]));
+    }
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kk = 0; kk < nK8; ++kk) asm volatile("" : "+a"(qf8[qb][kk]));
+      asm volatile("" : "+v"(qsc[qb]));
+    }
+  }
 
   // keys seen by the workgroup's last query, and by all of its queries
   const int kend = CAUSAL ? min(Tk, q0 + qrows + shift) : Tk;
@@ -441,6 +576,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     return row_operand<D>(Ks, (f / nK) * 32 + l32, 2 * (f % nK) + h);
   };
   auto v_frag = [&](const uint8_t* Vs, int g) { return tr_operand<D>(Vs, g % nD, 16 * (g / nD), lane); };
+  // E4M3 K fragment f = nK8 kb + kk: key row 32 kb + l32, the two 16-byte chunks of this lane
+  // half in k-step kk; and the row's scale bytes, shifted like the Q scales
+  auto k_frag8 = [&](const uint8_t* Ks, int f) {
+    const int row = (f / nK8) * 32 + l32, kk = f % nK8;
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(Ks + Tl8::offset(row, 4 * kk + h));
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(Ks + Tl8::offset(row, 4 * kk + 2 + h));
+    return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                 (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  };
+  auto k_scale = [&](const uint8_t* Ks, int kb) -> uint32_t {
+    const uint32_t sc = *reinterpret_cast<const uint32_t*>(Ks + Tl8::sc_offset + (32 * kb + l32) * 4);
+    return sc >> (8 * h);
+  };
 
   // ---- one pipelined iteration: tile j finishes, tile j+1 starts --------------------------
   // On entry: query block 0 of tile j is exponentiated, summed (tl, tr) and packed (pc);
@@ -455,27 +603,49 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     reset_max();
 
     // phase X: S of tile j+1 | query block 1 of tile j
-    bf16x8 kf[nKF];
-    kf[0] = k_frag(Kn, 0);
-    kf[1] = k_frag(Kn, 1);
+    bf16x8 kf[QK8 ? 1 : nKF];
+    i32x8 kf8[QK8 ? nKF8 : 1];
+    uint32_t ksc[2] = {0u, 0u};
+    if constexpr (!QK8) {
+      kf[0] = k_frag(Kn, 0);
+      kf[1] = k_frag(Kn, 1);
+    } else {
+      kf8[0] = k_frag8(Kn, 0);
+      kf8[1] = k_frag8(Kn, 1);
+      ksc[0] = k_scale(Kn, 0);
+      ksc[1] = k_scale(Kn, 1);
+      // the products read the scales a few instructions after the VALU shift wrote them
+      asm volatile("s_nop 4" : "+v"(ksc[0]), "+v"(ksc[1]));
+    }
     bf16x8 vf[nVF];
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, S::NX>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int f = i >> 1, qb = i & 1, kb = f / nK, kk = f % nK;
-      if constexpr (qb == 0 && f + 2 < nKF) kf[f + 2] = k_frag(Kn, f + 2);
+      if constexpr (!QK8 && qb == 0 && f + 2 < nKF) kf[f + 2] = k_frag(Kn, f + 2);
       // loads of K j+2 and V j+1, one per odd step (K j+2 is clamped into range past the last
       // tile: a harmless reload into a slot nobody reads any more)
-      if constexpr ((i & 1) && (i >> 1) < Tl::loadsPerWave)
-        ld.issue(kslot_p(jp, j, 2), Kh, (j + 2) * kBlockN, T, i >> 1);
-      if constexpr ((i & 1) && (i >> 1) >= Tl::loadsPerWave && (i >> 1) < 2 * Tl::loadsPerWave)
-        ld.issue(vslot_p(jp, j, 1), Vh, (j + 1) * kBlockN, T, (i >> 1) - Tl::loadsPerWave);
+      if constexpr ((i & 1) && (i >> 1) < LK) {
+        if constexpr (!QK8) ld.issue(kslot_p(jp, j, 2), Kh, (j + 2) * kBlockN, T, i >> 1);
+        else if constexpr ((i >> 1) < Tl8::loadsPerWave)
+          ld8.issue(kslot_p(jp, j, 2), Kh8, (j + 2) * kBlockN, T, i >> 1);
+        else ld8.issue_scales(kslot_p(jp, j, 2), Ksh, (j + 2) * kBlockN, T);
+      }
+      if constexpr ((i & 1) && (i >> 1) >= LK && (i >> 1) < LK + Tl::loadsPerWave)
+        ld.issue(vslot_p(jp, j, 1), Vh, (j + 1) * kBlockN, T, (i >> 1) - LK);
       if constexpr (i == S::NX - 2) {
         vf[0] = v_frag(Vs, 0);
         vf[1] = v_frag(Vs, 1);
       }
-      if constexpr (kk == 0) mfma_s_first(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
-      else mfma_s(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
+      if constexpr (!QK8) {
+        if constexpr (kk == 0) mfma_s_first(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
+        else mfma_s(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
+      } else if constexpr (i % 4 == 0) {
+        // one E4M3 product every fourth step: m = i / 4 -> query block m % 2, fragment m / 2
+        constexpr int m = i / 4, qb8 = m & 1, f8 = m >> 1, kb8 = f8 / nK8, kk8 = f8 % nK8;
+        if constexpr (qb8 == 0 && f8 + 2 < nKF8) kf8[f8 + 2] = k_frag8(Kn, f8 + 2);
+        mfma8_s<kk8 == 0, 2 * kk8>(sblk(nxt, qb8, kb8), kf8[f8], qf8[qb8][kk8], ksc[kb8], qsc[qb8]);
+      }
       if constexpr (i == S::XM0) fence2(sblk(nxt, 0, 0), sblk(nxt, 1, 0));
       static_for<32, 64>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
@@ -551,24 +721,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
   };
 
   // ---- prologue: tile 0's scores, max and query block 0 ---------------------------------
-  ld.issue_all(kslot(0), Kh, 0, T);
-  ld.issue_all(vslot(0), Vh, 0, T);
-  if (ntiles > 1) ld.issue_all(kslot(1), Kh, kBlockN, T);
+  if constexpr (!QK8) {
+    ld.issue_all(kslot(0), Kh, 0, T);
+    ld.issue_all(vslot(0), Vh, 0, T);
+    if (ntiles > 1) ld.issue_all(kslot(1), Kh, kBlockN, T);
+  } else {
+    ld8.issue_all(kslot(0), Kh8, Ksh, 0, T);
+    ld.issue_all(vslot(0), Vh, 0, T);
+    if (ntiles > 1) ld8.issue_all(kslot(1), Kh8, Ksh, kBlockN, T);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   {
     const uint8_t* K0 = kslot(0);
+    if constexpr (!QK8) {
 #pragma unroll
-    for (int f = 0; f < nKF; ++f) {
-      const bf16x8 a = k_frag(K0, f);
-      const int kb = f / nK, kk = f % nK;
-      if (kk == 0) {
-        mfma_s_first(s0[kb], a, qf[0][kk]);
-        mfma_s_first(s1a[kb], a, qf[1][kk]);
-      } else {
-        mfma_s(s0[kb], a, qf[0][kk]);
-        mfma_s(s1a[kb], a, qf[1][kk]);
+      for (int f = 0; f < nKF; ++f) {
+        const bf16x8 a = k_frag(K0, f);
+        const int kb = f / nK, kk = f % nK;
+        if (kk == 0) {
+          mfma_s_first(s0[kb], a, qf[0][kk]);
+          mfma_s_first(s1a[kb], a, qf[1][kk]);
+        } else {
+          mfma_s(s0[kb], a, qf[0][kk]);
+          mfma_s(s1a[kb], a, qf[1][kk]);
+        }
       }
+    } else {
+      uint32_t ksc0[2] = {k_scale(K0, 0), k_scale(K0, 1)};
+      asm volatile("s_nop 4" : "+v"(ksc0[0]), "+v"(ksc0[1]));
+      static_for<0, nKF8>([&](auto fc) {
+        constexpr int f = decltype(fc)::value, kb = f / nK8, kk = f % nK8;
+        const i32x8 a = k_frag8(K0, f);
+        mfma8_s<kk == 0, 2 * kk>(s0[kb], a, qf8[0][kk], ksc0[kb], qsc[0]);
+        mfma8_s<kk == 0, 2 * kk>(s1a[kb], a, qf8[1][kk], ksc0[kb], qsc[1]);
+      });
     }
     fence2(s0[0], s1a[0]);
     fence2(s0[1], s1a[1]);
@@ -638,9 +825,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool QK8>
 hipError_t launch(const FwdBf16Problem& p) {
   FwdKArgs k;
+  k.q8 = static_cast<const uint8_t*>(p.q8);
+  k.k8 = static_cast<const uint8_t*>(p.k8);
+  k.qs = static_cast<const uint8_t*>(p.q_scale);
+  k.ks = static_cast<const uint8_t*>(p.k_scale);
   k.q = static_cast<const uint16_t*>(p.q);
   k.k = static_cast<const uint16_t*>(p.k);
   k.v = static_cast<const uint16_t*>(p.v);
@@ -673,15 +864,19 @@ hipError_t launch(const FwdBf16Problem& p) {
     k.lse_bs = (int64_t)p.Hq * p.Tq;
   }
   k.c = p.scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QK8>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16_general(const FwdBf16Problem& p) {
-  if (p.D == 64) return p.causal ? launch<64, true>(p) : launch<64, false>(p);
-  return p.causal ? launch<128, true>(p) : launch<128, false>(p);
+  if (p.q8) {
+    if (p.D == 64) return p.causal ? launch<64, true, true>(p) : launch<64, false, true>(p);
+    return p.causal ? launch<128, true, true>(p) : launch<128, false, true>(p);
+  }
+  if (p.D == 64) return p.causal ? launch<64, true, false>(p) : launch<64, false, false>(p);
+  return p.causal ? launch<128, true, false>(p) : launch<128, false, false>(p);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {

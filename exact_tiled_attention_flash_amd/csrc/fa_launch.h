@@ -45,6 +45,9 @@ struct FwdBf16Problem {
   float scale;
   bool causal;
   hipStream_t stream;
+  // E4M3 Q K^T (null: bf16 q and k): codes laid out like q / k, one byte an element, and block
+  // scale bytes, one per 32 elements of a row; q and k are then ignored
+  const void *q8 = nullptr, *q_scale = nullptr, *k8 = nullptr, *k_scale = nullptr;
 };
 
 // Split-K decode: q, o (B, Hq, Tq, D) with G * Tq <= 32 (G = Hq / Hkv), k, v (B, Hkv, Tk, D),
@@ -68,6 +71,9 @@ hipError_t launch_fwd_bf16_general(const FwdBf16Problem &p);
 hipError_t launch_fwd_f32(const FwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a);
 hipError_t launch_decode_bf16(const DecodeBf16Problem &p);
+// Block-scaled E4M3 codes and scale bytes of `elems` bf16 values (elems a multiple of 32).
+hipError_t launch_quantize_mxfp8(const void *x, void *codes, void *scales, int64_t elems,
+                                 hipStream_t stream);
 int decode_max_splits();
 
 }  // namespace fa

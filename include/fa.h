@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 enum fa_dtype {
     FA_F32 = 0,
@@ -134,6 +134,42 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
                   const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq,
                   int Hkv, int total_q, int total_k, int max_seqlen_q, int D,
                   float scale, int causal, int dtype, void *stream);
+
+/*
+ * Block-scaled E4M3 quantization (FA_BF16 input only), the input of fa_fwd_fp8qk.
+ *   x       in:  rows x D bf16, contiguous (16-byte aligned); D a positive multiple of 32
+ *   codes   out: rows x D bytes (16-byte aligned), OCP E4M3: sign, 4 exponent bits (bias 7),
+ *                3 mantissa bits, subnormals m/8 * 2^-6, largest finite 448
+ *   scales  out: rows x (D / 32) bytes (4-byte aligned): for each block of 32 consecutive
+ *                elements of a row, 127 - e where e is the largest integer with
+ *                amax * 2^e <= 448 (amax the block's largest magnitude; e at most 127, and
+ *                0 for an all-zero block)
+ * Each element becomes the E4M3 value nearest to x * 2^e (ties to even) with the sign of x;
+ * the block's values are then code value * 2^(scale - 127). Inputs must be finite.
+ * A (B, H, T, D) tensor is rows = B * H * T.
+ * Source: "Lab 06 - Attention kernels", "Stretch" list (E4M3 Q and K for the Q K^T
+ * product); the format details and the power-of-two block scaling are this library's
+ * reading of what the page leaves open.
+ */
+int fa_quantize_mxfp8(const void *x, void *codes, void *scales, int rows, int D, int dtype,
+                      void *stream);
+
+/*
+ * Forward with E4M3 Q and K for the Q K^T product (bf16 V, P and output, fp32 statistics).
+ *   q8, q_scale  in: codes (B, Hq, Tq, D) bytes and scales (B, Hq, Tq, D / 32) bytes of Q,
+ *                as fa_quantize_mxfp8 writes them (codes 16-byte, scales 4-byte aligned)
+ *   k8, k_scale  in: the same for K, (B, Hkv, Tk, D) and (B, Hkv, Tk, D / 32)
+ *   v      in:  (B, Hkv, Tk, D) bf16
+ *   o      out: (B, Hq, Tq, D) bf16;  lse out: (B, Hq, Tq) float32
+ * S = scale * sum over blocks of (Q codes . K codes) * 2^(q scale - 127) * 2^(k scale - 127),
+ * on the gfx950 matrix cores' scaled E4M3 products with fp32 accumulation; everything after
+ * S is the bf16 forward's (heads, masking and lengths as fa_fwd_gqa).
+ * Source: "Lab 06 - Attention kernels", "Stretch" list (FP8 E4M3 Q and K for Q K^T,
+ * accuracy measured against speed).
+ */
+int fa_fwd_fp8qk(const void *q8, const void *q_scale, const void *k8, const void *k_scale,
+                 const void *v, void *o, float *lse, int B, int Hq, int Hkv, int Tq, int Tk,
+                 int D, float scale, int causal, void *stream);
 
 /*
  * Bytes of device workspace fa_fwd_decode needs for these sizes and this

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -194,3 +194,24 @@ def test_decode_validation(lib):
     assert decode(lib, splits=-1) == -7
     need = lib.fa_decode_workspace_bytes(2, 8, 2, 1, 64, 128, 0)
     assert decode(lib, ws=need - 1) == -7
+
+
+def test_quantize_validation(lib):
+    q = lambda x=P, c=P, s=P, rows=4, D=64, dtype=1: lib.fa_quantize_mxfp8(x, c, s, rows, D, dtype, None)
+    assert q(x=None) == -1 and q(c=None) == -1 and q(s=None) == -1
+    assert q(rows=0) == -2 and q(D=48) == -2 and q(D=0) == -2
+    assert q(rows=1 << 30, D=4096) == -2          # 2^42 elements
+    assert q(dtype=0) == -4
+    assert q(x=P + 8) == -5 and q(c=P + 4) == -5 and q(s=P + 2) == -5
+
+
+def test_fp8qk_validation(lib):
+    def f(nulls=(), Hq=4, Hkv=2, D=128, causal=1, scale=0.1, mis=None):
+        ptrs = [None if i in nulls else P for i in range(7)]
+        if mis is not None:
+            ptrs[mis[0]] = P + mis[1]
+        return lib.fa_fwd_fp8qk(*ptrs, 1, Hq, Hkv, 16, 16, D, ctypes.c_float(scale), causal, None)
+    for i in range(7):
+        assert f(nulls=(i,)) == -1
+    assert f(Hq=3) == -2 and f(D=96) == -3 and f(causal=2) == -7 and f(scale=float("inf")) == -6
+    assert f(mis=(0, 8)) == -5 and f(mis=(1, 2)) == -5 and f(mis=(2, 8)) == -5 and f(mis=(3, 2)) == -5
