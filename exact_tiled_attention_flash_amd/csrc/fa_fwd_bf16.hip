@@ -787,7 +787,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
     iteration(Par<1>{}, Par<0>{}, j + 1, Flag<false>{}, IC<1>{});
   }
-  // masked tail (at most five tiles): one body, the next tile's block-1 scores and block-0
+  // tile j + 1 may still need no mask (the pairs above stop one tile early): one more unmasked
+  // iteration, after which tile j + 1's buffers move to the even set the masked tail expects
+  if (j + 1 < nfull) {
+    iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
+    s1a[0] = s1b[0];
+    s1a[1] = s1b[1];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) p0a[cc] = p0b[cc];
+    ++j;
+  }
+  // masked tail (at most four tiles): one body, the next tile's block-1 scores and block-0
   // P are moved into the even buffers after each iteration so the roles never alternate
   for (; j + 1 < ntiles; ++j) {
     iteration(Par<0>{}, Par<1>{}, j, Flag<true>{}, IC<-1>{});
