@@ -24,7 +24,7 @@
 //     bound by HBM.
 //   * The partials go to the workspace as fp32: acc [split][M][D] and (m, l, l_rounded) per
 //     row, with m in the exp2 domain (scores times scale * log2 e). The merge kernel gives
-//     each output row one wave, lanes across D.
+//     each output row one workgroup of 256 threads, which read several splits at once.
 //   * As in the forward kernel, P is rounded to bf16 before the P V product; O is normalised
 //     by the sum of the rounded P and LSE uses the fp32 sum of the unrounded exponentials.
 
