@@ -18,8 +18,11 @@
 //     a tile sit in 32 registers of lane l and 32 of lane l ^ 32. The S^T accumulator
 //     layout is the B-operand layout of O^T += V^T P^T, so P never leaves registers; the
 //     V^T A operand is a transposing LDS read (ds_read_b64_tr_b16) of the row-major tile.
-//   * K and V tiles (64 keys) reach LDS by direct HBM -> LDS loads into XOR-swizzled
-//     row-major tiles, two slots each; K runs one tile ahead of V (see the pipeline).
+//   * K and V tiles (64 keys) reach LDS by direct buffer -> LDS loads into XOR-swizzled
+//     row-major tiles, two slots each; K runs one tile ahead of V (see the pipeline). The
+//     buffer resource ends at the last key row, so rows past it arrive as zeros and a load
+//     costs no vector arithmetic. The loads are inline asm, out of the compiler's sight:
+//     it would otherwise wait for every outstanding LDS read wherever it needs one of them.
 //   * exp(x) is exp2(x * scale * log2 e): one FMA and one v_exp_f32.
 //   * Lazy reference: a row's reference max m_ref moves only when a tile max exceeds it by
 //     more than 2^8 in the exp2 domain (and on the first tile), so P <= 2^8 and the O^T
@@ -112,8 +115,7 @@ struct SwzTile8 {
 template <int D>
 struct TileLoader8 {
   using Tl = SwzTile8<D>;
-  int row[Tl::loadsPerWave];
-  uint32_t cofs[Tl::loadsPerWave];
+  uint32_t vofs[Tl::loadsPerWave];   // byte offset of the lane's i-th chunk from the tile's row 0
   int wave, lane;
   uint32_t rsb, srs;   // bytes between rows of the codes and of the scales
   __device__ __forceinline__ TileLoader8(int wave_, int lane_, int row_stride)
@@ -121,28 +123,27 @@ struct TileLoader8 {
 #pragma unroll
     for (int i = 0; i < Tl::loadsPerWave; ++i) {
       const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
-      row[i] = u / Tl::CH;
-      cofs[i] = (uint32_t)(((u % Tl::CH) ^ Tl::swz(row[i])) * 16);
+      const int row = u / Tl::CH;
+      vofs[i] = (uint32_t)row * rsb + (uint32_t)(((u % Tl::CH) ^ Tl::swz(row)) * 16);
     }
   }
-  __device__ __forceinline__ void issue(uint8_t* dst, const uint8_t* __restrict__ src, int row0,
-                                        int T, int i) const {
-    const uint32_t off = (uint32_t)min(row0 + row[i], T - 1) * rsb + cofs[i];
-    __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(dst + (wave * Tl::loadsPerWave + i) * 1024),
-                                     16, 0, 0);
+  // codes and scales come through buffer resources over the T rows (rows at or past T: zeros)
+  __device__ __forceinline__ void issue(uint8_t* dst, const i32x4& rsrc, int row0, int T,
+                                        int i) const {
+    buf_lds_dma<16>(dst + (wave * Tl::loadsPerWave + i) * 1024, rsrc, vofs[i],
+                    (uint32_t)min(row0, T) * rsb);
   }
-  __device__ __forceinline__ void issue_scales(uint8_t* dst, const uint8_t* __restrict__ src,
-                                               int row0, int T) const {
-    if (wave == 0) {
-      const uint32_t off = (uint32_t)min(row0 + lane, T - 1) * srs;
-      __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(dst + Tl::sc_offset), Tl::SB, 0, 0);
-    }
+  __device__ __forceinline__ void issue_scales(uint8_t* dst, const i32x4& srsrc, int row0,
+                                               int T) const {
+    if (wave == 0)
+      buf_lds_dma<Tl::SB>(dst + Tl::sc_offset, srsrc, (uint32_t)lane * srs,
+                          (uint32_t)min(row0, T) * srs);
   }
-  __device__ __forceinline__ void issue_all(uint8_t* dst, const uint8_t* __restrict__ src,
-                                            const uint8_t* __restrict__ ssrc, int row0, int T) const {
+  __device__ __forceinline__ void issue_all(uint8_t* dst, const i32x4& rsrc, const i32x4& srsrc,
+                                            int row0, int T) const {
 #pragma unroll
-    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, src, row0, T, i);
-    issue_scales(dst, ssrc, row0, T);
+    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, rsrc, row0, T, i);
+    issue_scales(dst, srsrc, row0, T);
   }
 };
 // 20 wait states (more than the result latency of a 32x32x16 product) between the last
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
   float* Lh = args.lse + b * args.lse_bs + hq * args.lse_hs + qs;
   const uint16_t* Kh = args.k + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
   const uint16_t* Vh = args.v + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
-  const int T = Tk;   // key rows of this sequence (tile loads clamp to T - 1)
+  const int T = Tk;   // key rows of this sequence (tile rows at or past T load as zeros)
   auto kslot = [&](int t) -> uint8_t* { return (t & 1) ? ks1 : ks0; };
   auto vslot = [&](int t) -> uint8_t* { return (t & 1) ? vs1 : vs0; };
   // jp: parity of j as IC<0> / IC<1>, or IC<-1> when only known at run time
@@ -348,13 +349,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     if constexpr (P < 0) return vslot(j + d);
     else return ((P + d) & 1) ? vs1 : vs0;
   };
-  const TileLoader<D> ld(wave, lane, args.kv_rs);
+  const BufTileLoader<D> ld(wave, lane, args.kv_rs);
   const TileLoader8<D> ld8(wave, lane, args.kv_rs);
-  const uint8_t *Kh8 = nullptr, *Ksh = nullptr;
+  // buffer resources over this head's T key rows (one head stays below 2^31 bytes)
+  const uint32_t kv_bytes = (uint32_t)T * (uint32_t)args.kv_rs * 2u;
+  const i32x4 Kr = rows_rsrc(Kh, kv_bytes), Vr = rows_rsrc(Vh, kv_bytes);
+  i32x4 Kr8 = Kr, Ksr = Kr;
   if constexpr (QK8) {
     const int64_t ko = b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
-    Kh8 = args.k8 + ko;
-    Ksh = args.ks + ko / 32;
+    Kr8 = rows_rsrc(args.k8 + ko, kv_bytes / 2u);
+    Ksr = rows_rsrc(args.ks + ko / 32, kv_bytes / 64u);
   }
 
   // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
@@ -497,7 +501,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
       x[2 * t] = a;
       x[2 * t + 1] = b;
     }
-    pm[qb][kb] = fmaxf(pm[qb][kb], fmaxf(a, b));
+    // one v_max3 per pair (left to itself the compiler reassociates the chain into a tree
+    // of twice as many instructions); the scores' producers are fenced before the first item
+    float m = pm[qb][kb];
+    asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b));
+    pm[qb][kb] = m;
   };
   auto exp_item = [&](auto par, int v, bool masked) {
     const int qb = v >> 5, kb = (v >> 4) & 1, r = v & 15;
@@ -506,9 +514,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     const float e = exp2_fast(fmaf(x, c, -mc[qb]));
     blk[r] = (masked && x == kNegInf) ? 0.f : e;
   };
+  // The sums are pinned to their step with an empty asm that takes them as operands:
+  // otherwise the compiler sinks the whole chain of additions to the end of the iteration,
+  // where it runs as one block with no product to hide under.
   auto sum_item = [&](auto par, int v) {
     const int qb = v >> 5, kb = (v >> 4) & 1, r = v & 15;
     tl[qb][kb] += sblk(par, qb, kb)[r];
+    asm volatile("" : "+v"(tl[qb][kb]));
   };
   // Pack chunk ch to the bf16 B operand and add the rounded values. The words are summed
   // before they are gathered into the operand vector: with this toolchain,
@@ -523,6 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     tr[qb][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tr[qb][1], false);
     tr[qb][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, tr[qb][0], false);
     tr[qb][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, tr[qb][1], false);
+    asm volatile("" : "+v"(tr[qb][0]), "+v"(tr[qb][1]));
     pop(ppar, qb, cc) = as_bf16x8(u32x4{w0, w1, w2, w3});
   };
   // the finished tile's sums join the running sums (same reference by now)
@@ -623,16 +636,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
       constexpr int i = decltype(ic)::value;
       constexpr int f = i >> 1, qb = i & 1, kb = f / nK, kk = f % nK;
       if constexpr (!QK8 && qb == 0 && f + 2 < nKF) kf[f + 2] = k_frag(Kn, f + 2);
-      // loads of K j+2 and V j+1, one per odd step (K j+2 is clamped into range past the last
-      // tile: a harmless reload into a slot nobody reads any more)
+      // loads of K j+2 and V j+1, one per odd step (past the last tile, K j+2 loads zeros
+      // into a slot nobody reads any more)
       if constexpr ((i & 1) && (i >> 1) < LK) {
-        if constexpr (!QK8) ld.issue(kslot_p(jp, j, 2), Kh, (j + 2) * kBlockN, T, i >> 1);
+        if constexpr (!QK8) ld.issue(kslot_p(jp, j, 2), Kr, (j + 2) * kBlockN, T, i >> 1);
         else if constexpr ((i >> 1) < Tl8::loadsPerWave)
-          ld8.issue(kslot_p(jp, j, 2), Kh8, (j + 2) * kBlockN, T, i >> 1);
-        else ld8.issue_scales(kslot_p(jp, j, 2), Ksh, (j + 2) * kBlockN, T);
+          ld8.issue(kslot_p(jp, j, 2), Kr8, (j + 2) * kBlockN, T, i >> 1);
+        else ld8.issue_scales(kslot_p(jp, j, 2), Ksr, (j + 2) * kBlockN, T);
       }
       if constexpr ((i & 1) && (i >> 1) >= LK && (i >> 1) < LK + Tl::loadsPerWave)
-        ld.issue(vslot_p(jp, j, 1), Vh, (j + 1) * kBlockN, T, (i >> 1) - LK);
+        ld.issue(vslot_p(jp, j, 1), Vr, (j + 1) * kBlockN, T, (i >> 1) - LK);
       if constexpr (i == S::NX - 2) {
         vf[0] = v_frag(Vs, 0);
         vf[1] = v_frag(Vs, 1);
@@ -722,13 +735,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
 
   // ---- prologue: tile 0's scores, max and query block 0 ---------------------------------
   if constexpr (!QK8) {
-    ld.issue_all(kslot(0), Kh, 0, T);
-    ld.issue_all(vslot(0), Vh, 0, T);
-    if (ntiles > 1) ld.issue_all(kslot(1), Kh, kBlockN, T);
+    ld.issue_all(kslot(0), Kr, 0, T);
+    ld.issue_all(vslot(0), Vr, 0, T);
+    if (ntiles > 1) ld.issue_all(kslot(1), Kr, kBlockN, T);
   } else {
-    ld8.issue_all(kslot(0), Kh8, Ksh, 0, T);
-    ld.issue_all(vslot(0), Vh, 0, T);
-    if (ntiles > 1) ld8.issue_all(kslot(1), Kh8, Ksh, kBlockN, T);
+    ld8.issue_all(kslot(0), Kr8, Ksr, 0, T);
+    ld.issue_all(vslot(0), Vr, 0, T);
+    if (ntiles > 1) ld8.issue_all(kslot(1), Kr8, Ksr, kBlockN, T);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

@@ -10,6 +10,45 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes from `base` (raw: no stride, no format conversion). A
+// load whose offset (voffset + soffset) lies at or past `bytes` returns zeros without touching
+// memory, and a direct-to-LDS load writes those zeros, so tiles reaching past the last row of
+// a matrix need no address clamping.
+__device__ __forceinline__ i32x4 rows_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// Direct buffer -> LDS load of BYTES (16, 4 or 2) bytes a lane from voff + soff, written as
+// inline asm so that the compiler does not track it. (It models a direct-to-LDS load as an
+// LDS access that may complete out of order with the LDS reads, and from then on waits for all
+// outstanding LDS reads wherever it needs any one of them.) The hardware counts the load in
+// vmcnt only: the caller waits with s_waitcnt vmcnt, and a barrier for the other waves, before
+// the destination is read. Lane l writes 16 bytes (BYTES = 16) or one zero-extended dword at
+// LDS byte lds + 16 l (or + 4 l); `lds`, `rsrc` and `soff` are wave-uniform. M0 carries the
+// LDS address and is set inside the same statement.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int BYTES>
+__device__ __forceinline__ void buf_lds_dma(void* lds, const i32x4& rsrc, uint32_t voff,
+                                            uint32_t soff) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void*)lds;
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(a), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  else if constexpr (BYTES == 4)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(a), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  else {
+    static_assert(BYTES == 2, "buf_lds_dma size");
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+                 :: "s"(a), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  }
+}
+#pragma clang diagnostic pop
+
 // A [64 x D] bf16 tile stored unpadded; the 16-byte chunks of a row are XOR-swizzled. Two
 // read patterns must spread over the LDS banks: (a) a 16-byte read by lanes holding
 // consecutive rows of one logical chunk (8 rows per LDS cycle with 32 four-byte banks, 16
@@ -72,6 +111,36 @@ struct TileLoader {
                                             int T) const {
 #pragma unroll
     for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, src, row0, T, i);
+  }
+};
+
+// The loads of TileLoader through a buffer resource over the source's T rows (rows_rsrc):
+// each lane's offset within the tile is fixed, the tile's first row goes into the scalar
+// offset, and rows at or past T arrive as zeros. No per-load vector arithmetic remains.
+template <int D>
+struct BufTileLoader {
+  using Tl = SwzTile<D>;
+  uint32_t vofs[Tl::loadsPerWave];   // byte offset of the lane's i-th chunk from the tile's row 0
+  int wave;
+  uint32_t rsb;                      // bytes between consecutive rows of the source matrix
+  __device__ __forceinline__ BufTileLoader(int wave_, int lane, int row_stride = D)
+      : wave(wave_), rsb((uint32_t)row_stride * 2u) {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) {
+      const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
+      const int row = u / Tl::CH;
+      vofs[i] = (uint32_t)row * rsb + (uint32_t)(((u % Tl::CH) ^ Tl::swz(row)) * 16);
+    }
+  }
+  // load i of rows [row0, row0 + 64) of the resource's matrix (T rows) into the tile at dst
+  __device__ __forceinline__ void issue(uint8_t* dst, const i32x4& rsrc, int row0, int T,
+                                        int i) const {
+    buf_lds_dma<16>(dst + (wave * Tl::loadsPerWave + i) * 1024, rsrc, vofs[i],
+                    (uint32_t)min(row0, T) * rsb);
+  }
+  __device__ __forceinline__ void issue_all(uint8_t* dst, const i32x4& rsrc, int row0, int T) const {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, rsrc, row0, T, i);
   }
 };
 
