@@ -81,20 +81,28 @@ def _time_loop(torch, fn, steps, warmup):
 
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_b4h16t4096d128_causal_traffic.json")
-FWD_SOURCE = os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc", "fa_fwd_bf16.hip")
+# the sources the headline forward kernel is compiled from
+FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc", f)
+               for f in ("fa_fwd_bf16_q32.hip", "fa_fwd_parts.h", "fa_swz.h", "fa_common.h")]
+
+
+def fwd_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FWD_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def committed_traffic(flops):
     """HBM bytes per launch of the forward kernel from the committed rocprofv3 FETCH_SIZE and
     WRITE_SIZE runs (scaled by the same counters on a copy of known size), provided the kernel
     source is unchanged since they were taken; else None."""
-    import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    digest = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != digest:
+    if rec.get("kernel_source_sha256") != fwd_source_digest():
         return None
     return {"bytes_per_launch": rec["hbm_bytes_per_launch"], "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
 
@@ -293,7 +301,7 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "fwd_bf16_kernel<128, causal>",
+                     "kernel": "fwd_q32_kernel<128, causal>",
                      "avg_launch_ms": round(avg_launch_ms, 5),
                      "min_launch_ms": round(float(np.min(per)), 5),
                      "median_launch_ms": round(float(np.median(per)), 5),

@@ -1,0 +1,548 @@
+// Attention forward, bf16 storage, fp32 accumulation, with two workgroups on every compute
+// unit: hand-written gfx950 kernel.
+//
+// Method: the same as the other bf16 forward kernel. "Lab 06 - Attention kernels", section 3
+// (per query tile keep the row max m, row sum l and accumulator acc; per key tile rescale by
+// exp(m - m') and add exp(S - m') V; finish with O = acc / l and LSE = m + log l; causal
+// tiles above the diagonal are never loaded, diagonal tiles are masked element-wise) and
+// section 5 (one program per (query tile, batch*head)). "Triton FlashAttention-2 forward",
+// "The kernel" (P rounded to the input dtype before the P V product, masked loads read zeros
+// beyond T). Section 2 of the lab page: subtracting any constant from the exponents and
+// dividing it back out is exact, which the lazy reference relies on.
+//
+// gfx950 mapping
+//   * A wave issues a 32x32x16 product in about 12 cycles of its own time and the product
+//     occupies the matrix core for 32, so one wave per SIMD leaves the matrix core idle while
+//     it works through the softmax. Here every wave holds one block of 32 queries (O^T in 64
+//     AGPRs, Q^T in 32), a wave needs at most 256 registers, and two workgroups of 4 waves
+//     share each compute unit: the SIMD runs one wave's products while the other wave's
+//     vector instructions issue.
+//   * Workgroup: 4 waves, 128 queries of one (b, h) (or 128 / hpw queries of hpw heads that
+//     share a K/V head). K and V tiles of 64 keys reach LDS by direct buffer -> LDS loads
+//     (two slots each, 64 KB a workgroup); rows past the last key arrive as zeros.
+//   * S^T = K Q^T puts one query per lane; a row's 64 scores of a tile sit in two 16-register
+//     blocks (key halves kb = 0, 1) of lanes l and l ^ 32. The S^T accumulator layout is the
+//     B-operand layout of O^T += V^T P^T, so P never leaves registers.
+//   * Software pipeline across key tiles: phase X of iteration j runs the S products of tile
+//     j+1 while the VALU finishes key half 1 of tile j (exponentials, fp32 and rounded sums,
+//     packing) and takes the max over key half 0 of tile j+1; phase Y runs tile j's P V
+//     products while the VALU takes the max over key half 1 of tile j+1, moves the
+//     references and works through key half 0 of tile j+1. Each step of a phase holds one
+//     product followed by a fixed share of the VALU work, fenced with sched_barrier.
+//   * Lazy reference max (moves only when exceeded by more than 2^8 in the exp2 domain), O
+//     normalised by the sum of the bf16-rounded P, LSE from the fp32 sum of the unrounded
+//     exponentials, as in the other forward kernel.
+
+#include "fa_common.h"
+#include "fa_launch.h"
+#include "fa_swz.h"
+#include "fa_fwd_parts.h"
+
+namespace fa {
+namespace {
+
+using namespace fwd;
+
+constexpr int kThreads = 256;
+constexpr int kBlockM = 128;   // queries per workgroup, 32 per wave
+
+// 20 wait states between the last product writing x and any later instruction that uses it.
+__device__ __forceinline__ void fence1(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x));
+}
+
+// ---- per-step work assignment (all compile-time) --------------------------------------
+// Items of one tile: 32 score elements per lane, v = 16 kb + r; 4 chunks of 8 (v / 8 = ch,
+// the B operand P[ch] of keys 16 ch .. 16 ch + 15); 8 max items per key half (pairs of
+// elements). Key half 0 of a tile is finished in phase Y of the iteration before the one
+// that multiplies it, key half 1 in phase X of that iteration.
+template <int D>
+struct Sched1 {
+  static constexpr int nK = D / 16, nD = D / 32;
+  static constexpr int NX = 2 * nK;   // phase X steps (S products, f = nK kb + kk)
+  static constexpr int NY = 4 * nD;   // phase Y steps (P V products, g = nD cc + db)
+  static constexpr int XE0 = 0, XE1 = NX - 4, XS0 = 1, XS1 = NX - 2;
+  static constexpr int XM0 = nK + 2, XM1 = NX;
+  static constexpr int YM0 = 2, YM1 = 2 + NY / 8, YR = YM1, YE0 = YR + 1, YE1 = NY - 2;
+  static constexpr int YS0 = YE0 + 1, YS1 = NY;
+  static constexpr int x_exp(int v) { return win_step(v - 16, 16, XE0, XE1); }   // v in [16, 32)
+  static constexpr int x_sum(int v) { return win_step(v - 16, 16, XS0, XS1); }
+  static constexpr int x_pack(int ch) { return x_exp(8 * ch + 7) + 1; }            // ch = 2, 3
+  static constexpr int XF = (x_sum(31) > x_pack(3) ? x_sum(31) : x_pack(3)) + 1;
+  static constexpr int x_max(int t) { return win_step(t, 8, XM0, XM1); }           // kb = 0
+  static constexpr int y_max(int t) { return win_step(t, 8, YM0, YM1); }           // kb = 1
+  static constexpr int y_exp(int v) { return win_step(v, 16, YE0, YE1); }          // v in [0, 16)
+  static constexpr int y_sum(int v) { return win_step(v, 16, YS0, YS1); }
+  // chunk ch (0, 1) of the next tile overwrites P[ch] one step after this tile's last product
+  // that reads it (steps nD ch .. nD ch + nD - 1)
+  static constexpr int y_pack(int ch) {
+    return y_exp(8 * ch + 7) + 1 > nD * (ch + 1) + 1 ? y_exp(8 * ch + 7) + 1 : nD * (ch + 1) + 1;
+  }
+  static constexpr bool valid() {
+    for (int v = 0; v < 16; ++v)
+      if (y_sum(v) <= y_exp(v) || y_sum(v) >= NY) return false;
+    for (int v = 16; v < 32; ++v)
+      if (x_sum(v) <= x_exp(v) || x_sum(v) >= NX) return false;
+    return YR < YE0 && XF < NX && y_max(7) < YR && y_pack(1) < NY && x_pack(3) < NX &&
+           XM0 > nK && x_max(7) < NX;
+  }
+};
+static_assert(Sched1<128>::valid() && Sched1<64>::valid(), "pipeline schedule order");
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs args) {
+  using Tl = SwzTile<D>;
+  using S = Sched1<D>;
+  constexpr int nD = D / 32;   // 32-row blocks of O^T
+  constexpr int nK = D / 16;   // k-steps of S^T = K Q^T
+  constexpr int NX = S::NX, NY = S::NY;
+  constexpr int LK = Tl::loadsPerWave;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[Tl::bytes], ks1[Tl::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[Tl::bytes], vs1[Tl::bytes];
+
+  const int tid = lane_thread_id();
+  const int wave = wave_id();
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  const float c = args.c;
+  // Workgroup -> (query tile, batch, head group): heaviest causal tiles first, (batch, head
+  // group) fastest. hpw query heads sharing one K/V head, 128 / hpw consecutive queries each.
+  const int L = workgroup_id();
+  const int r = L % args.nbhg;
+  int qt = L / args.nbhg;
+  if (CAUSAL) qt = args.nq - 1 - qt;
+  const int b = r / args.HG, hg = r % args.HG;
+  const int hpw = 1 << args.hpw_log2;
+  const int h0 = hg * hpw;
+  const int hq = h0 + (wave & (hpw - 1));   // this wave's query head
+  const int kvh = h0 / args.G;
+  const int qrows = kBlockM >> args.hpw_log2;
+  int qs = 0, Tq = args.Tq, ks = 0, Tk = args.Tk;
+  if (args.cu_q) {
+    qs = min(max(args.cu_q[b], 0), args.Tq);
+    Tq = min(max(args.cu_q[b + 1], qs), args.Tq) - qs;
+    ks = min(max(args.cu_k[b], 0), args.Tk);
+    Tk = min(max(args.cu_k[b + 1], ks), args.Tk) - ks;
+    qs = __builtin_amdgcn_readfirstlane(qs);
+    Tq = __builtin_amdgcn_readfirstlane(Tq);
+    ks = __builtin_amdgcn_readfirstlane(ks);
+    Tk = __builtin_amdgcn_readfirstlane(Tk);
+  }
+  const int q0 = qt * qrows;
+  if (q0 >= Tq) return;   // uniform per workgroup
+  const int qw0 = q0 + (wave >> args.hpw_log2) * 32;   // this wave's first query
+  const int shift = CAUSAL ? Tk - Tq : 0;              // bottom-right alignment
+  const int qrow = qw0 + l32;                          // this lane's query
+
+  const uint16_t* Qh = args.q + b * args.q_bs + (int64_t)qs * args.q_rs + hq * args.q_hs;
+  uint16_t* Oh = args.o + b * args.q_bs + (int64_t)qs * args.q_rs + hq * args.q_hs;
+  float* Lh = args.lse + b * args.lse_bs + hq * args.lse_hs + qs;
+  const uint16_t* Kh = args.k + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
+  const uint16_t* Vh = args.v + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
+  const int T = Tk;
+  auto kslot = [&](int t) -> uint8_t* { return (t & 1) ? ks1 : ks0; };
+  auto vslot = [&](int t) -> uint8_t* { return (t & 1) ? vs1 : vs0; };
+  auto kslot_p = [&](auto jp, int j, int d) -> uint8_t* {
+    constexpr int P = decltype(jp)::value;
+    if constexpr (P < 0) return kslot(j + d);
+    else return ((P + d) & 1) ? ks1 : ks0;
+  };
+  auto vslot_p = [&](auto jp, int j, int d) -> uint8_t* {
+    constexpr int P = decltype(jp)::value;
+    if constexpr (P < 0) return vslot(j + d);
+    else return ((P + d) & 1) ? vs1 : vs0;
+  };
+  const BufTileLoader<D> ld(wave, lane, args.kv_rs);
+  const uint32_t kv_bytes = (uint32_t)T * (uint32_t)args.kv_rs * 2u;
+  const i32x4 Kr = rows_rsrc(Kh, kv_bytes), Vr = rows_rsrc(Vh, kv_bytes);
+
+  // Q^T fragments: lane holds query qrow, d = 16 kk + 8 h + 0..7; moved into AGPRs
+  bf16x8 qf[nK];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) {
+    u32x4 x = qrow < Tq ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
+    qf[kk] = as_bf16x8(x);
+  }
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[kk]));
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[kk]));
+
+  // keys seen by the workgroup's last query, and by all of its queries
+  const int kend = CAUSAL ? min(Tk, q0 + qrows + shift) : Tk;
+  const int ntiles = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  const int kall = CAUSAL ? min(Tk, q0 + shift + 1) : Tk;
+  const int nfull = kall > 0 ? min(kall / kBlockN, ntiles) : 0;
+
+  if (ntiles == 0) {   // no query of this workgroup sees a key
+    if (qrow < Tq) {
+      uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
+#pragma unroll
+      for (int d0 = 0; d0 < D; d0 += 8)
+        if ((d0 / 8) % 2 == h) *reinterpret_cast<u32x4*>(orow + d0) = u32x4{0u, 0u, 0u, 0u};
+      if (h == 0) Lh[qrow] = kNegInf;
+    }
+    return;
+  }
+
+  f32x16 acc[nD];
+#pragma unroll
+  for (int db = 0; db < nD; ++db) acc[db] = f32x16{};
+  float m_ref, mc;                  // reference max (raw score units) and m_ref * c
+  // row sums per key half: fp32 exponentials (l) and bf16-rounded P (r, two chains), for the
+  // tiles already folded in (lp, rp) and for the tile in progress (tl, tr)
+  float lp[2] = {0.f, 0.f}, rp[2] = {0.f, 0.f}, tl[2] = {0.f, 0.f}, tr[2] = {0.f, 0.f};
+  float pm[2];                      // partial row maxima of the next tile, per key half
+  // scores: key half 0 (one buffer) and key half 1 (two, by tile parity); P chunks 0-3
+  f32x16 s0, s1a, s1b;
+  bf16x8 p[4];
+  auto sblk = [&](auto par, int kb) -> f32x16& {
+    if constexpr (decltype(par)::value == 0) return kb ? s1a : s0;
+    else return kb ? s1b : s0;
+  };
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+
+  // element r of key half kb is key 32 kb + 8 (r / 4) + (r % 4) + 4 h of the tile; it is
+  // valid iff that local index is below the returned limit
+  auto tile_lim = [&](int t) {
+    const int k0 = t * kBlockN;
+    int l = Tk - k0;
+    if (CAUSAL) l = min(l, qrow + shift - k0 + 1);
+    return l - 4 * h;
+  };
+
+  // ---- work items ------------------------------------------------------------------------
+  auto max_item = [&](auto par, int kb, int t, bool masked, int lim) {
+    f32x16& x = sblk(par, kb);
+    float a = x[2 * t], b2 = x[2 * t + 1];
+    if (masked) {
+      const int kla = 32 * kb + 8 * (t >> 1) + 2 * (t & 1);
+      a = kla < lim ? a : kNegInf;
+      b2 = kla + 1 < lim ? b2 : kNegInf;
+      x[2 * t] = a;
+      x[2 * t + 1] = b2;
+    }
+    float m = pm[kb];
+    asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b2));
+    pm[kb] = m;
+  };
+  auto exp_item = [&](auto par, int v, bool masked) {
+    const int kb = v >> 4, rr = v & 15;
+    f32x16& blk = sblk(par, kb);
+    const float x = blk[rr];
+    float e = exp2_fast(fmaf(x, c, -mc));
+    e = (masked && x == kNegInf) ? 0.f : e;
+    asm volatile("" : "+v"(e));   // keeps the exponential at its step
+    blk[rr] = e;
+  };
+  auto sum_item = [&](auto par, int v) {
+    const int kb = v >> 4, rr = v & 15;
+    tl[kb] += sblk(par, kb)[rr];
+    asm volatile("" : "+v"(tl[kb]));
+  };
+  // pack chunk ch to the bf16 B operand P[ch] and add the rounded values
+  auto pack_item = [&](auto par, int ch) {
+    const int kb = ch >> 1, o = (ch & 1) * 8;
+    const f32x16& sv = sblk(par, kb);
+    const uint32_t w0 = pack_bf16x2(sv[o + 0], sv[o + 1]), w1 = pack_bf16x2(sv[o + 2], sv[o + 3]);
+    const uint32_t w2 = pack_bf16x2(sv[o + 4], sv[o + 5]), w3 = pack_bf16x2(sv[o + 6], sv[o + 7]);
+    tr[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, tr[0], false);
+    tr[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tr[1], false);
+    tr[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, tr[0], false);
+    tr[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, tr[1], false);
+    asm volatile("" : "+v"(tr[0]), "+v"(tr[1]));
+    p[ch] = as_bf16x8(u32x4{w0, w1, w2, w3});
+  };
+  auto fold = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lp[i] += tl[i];
+      rp[i] += tr[i];
+      tl[i] = 0.f;
+      tr[i] = 0.f;
+    }
+  };
+  // full-row max of the next tile; moves the references (every row of the wave, when any row
+  // exceeds its reference by more than the margin) and says whether a rescale is due
+  auto reduce = [&](float& m_old) {
+    const float a = halves_max1(fmaxf(pm[0], pm[1]));
+    const bool need = (a - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
+    const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+    m_old = m_ref;
+    m_ref = any ? fmaxf(m_ref, a) : m_ref;
+    mc = m_ref * c;
+    return any;
+  };
+  auto rescale = [&](float m_old) {
+    const float alpha = m_old == m_ref ? 1.f : exp2_fast((m_old - m_ref) * c);
+#pragma unroll
+    for (int db = 0; db < nD; ++db) acc[db] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lp[i] *= alpha;
+      rp[i] *= alpha;
+    }
+  };
+  // Operand reads from a tile: only the in-row part of an address depends on the lane and the
+  // k-step, so it is kept per k-step (koff) or per 32-column block of V (voff); the key-half
+  // and 16-key chunk steps (32 and 16 rows) leave the swizzle unchanged and become constant
+  // offsets. K fragment f = nK kb + kk: 8 bf16 of key row 32 kb + l32, logical chunk 2 kk + h.
+  // V^T fragment g = nD cc + db: as tr_operand with kbase = 16 cc.
+  uint32_t koff[nK], voff[nD][2];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) koff[kk] = (uint32_t)Tl::offset(l32, 2 * kk + h);
+  {
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int row = 4 * (g4 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < nD; ++db) {
+      const int d0 = db * 32 + (g4 & 1) * 16 + 4 * (i16 & 3);
+      voff[db][0] = (uint32_t)(Tl::offset(row, d0 >> 3) + (d0 & 7) * 2);
+      voff[db][1] = (uint32_t)(Tl::offset(row + 8, d0 >> 3) + (d0 & 7) * 2);
+    }
+  }
+  auto k_frag = [&](const uint8_t* Ks, int f) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (f / nK) * 32 * Tl::RB + koff[f % nK]));
+  };
+  auto v_frag = [&](const uint8_t* Vs, int g) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint8_t* base = Vs + (g / nD) * 16 * Tl::RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[g % nD][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[g % nD][1]));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  // ---- one pipelined iteration: tile j finishes, tile j+1 starts --------------------------
+  // On entry: key half 0 of tile j is exponentiated, summed and packed (P[0], P[1]); cur holds
+  // key half 1's scores; tile j+1's K is in kslot(j+1), tile j's V in vslot(j).
+  auto iteration = [&](auto cur, auto nxt, int j, auto mask_tag, auto jp) {
+    constexpr bool MASK = decltype(mask_tag)::value;   // tile j+1 may need masks
+    const int lim = MASK ? tile_lim(j + 1) : 0;
+    const uint8_t* Kn = kslot_p(jp, j, 1);
+    const uint8_t* Vs = vslot_p(jp, j, 0);
+    pm[0] = pm[1] = kNegInf;
+
+    // phase X: S of tile j+1 | key half 1 of tile j
+    bf16x8 kf[NX];
+    kf[0] = k_frag(Kn, 0);
+    kf[1] = k_frag(Kn, 1);
+    bf16x8 vf[NY];
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NX>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int kb = i / nK, kk = i % nK;
+      if constexpr (i + 2 < NX) kf[i + 2] = k_frag(Kn, i + 2);
+      // loads of K j+2 and V j+1, one per odd step (past the last tile, K j+2 loads zeros
+      // into a slot nobody reads any more)
+      if constexpr ((i & 1) && (i >> 1) < LK) ld.issue(kslot_p(jp, j, 2), Kr, (j + 2) * kBlockN, T, i >> 1);
+      if constexpr ((i & 1) && (i >> 1) >= LK && (i >> 1) < 2 * LK)
+        ld.issue(vslot_p(jp, j, 1), Vr, (j + 1) * kBlockN, T, (i >> 1) - LK);
+      if constexpr (i == NX - 2) {
+        vf[0] = v_frag(Vs, 0);
+        vf[1] = v_frag(Vs, 1);
+      }
+      if constexpr (kk == 0) mfma_s_first(sblk(nxt, kb), kf[i], qf[kk]);
+      else mfma_s(sblk(nxt, kb), kf[i], qf[kk]);
+      // the step's VALU work follows its product, so consecutive products are evenly spaced
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == S::XM0) fence1(sblk(nxt, 0));
+      static_for<16, 32>([&](auto vc) {
+        constexpr int v = decltype(vc)::value;
+        if constexpr (S::x_exp(v) == i) exp_item(cur, v, MASK);
+        if constexpr (S::x_sum(v) == i) sum_item(cur, v);
+      });
+      static_for<2, 4>([&](auto cc_) {
+        constexpr int ch = decltype(cc_)::value;
+        if constexpr (S::x_pack(ch) == i) pack_item(cur, ch);
+      });
+      if constexpr (i == S::XF) fold();
+      static_for<0, 8>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (S::x_max(t) == i) max_item(nxt, 0, t, MASK, lim);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // phase Y: P V of tile j | max, reference update and key half 0 of tile j+1
+    float m_old = 0.f;
+    bool any = false;
+    static_for<0, NY>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int cc = i / nD, db = i % nD;
+      if constexpr (i + 2 < NY) vf[i + 2] = v_frag(Vs, i + 2);
+      mfma_o(acc[db], vf[i], p[cc]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == S::YM0) fence1(sblk(nxt, 1));
+      static_for<0, 8>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (S::y_max(t) == i) max_item(nxt, 1, t, MASK, lim);
+      });
+      if constexpr (i == S::YR) any = reduce(m_old);
+      static_for<0, 16>([&](auto vc) {
+        constexpr int v = decltype(vc)::value;
+        if constexpr (S::y_exp(v) == i) exp_item(nxt, v, MASK);
+        if constexpr (S::y_sum(v) == i) sum_item(nxt, v);
+      });
+      static_for<0, 2>([&](auto cc_) {
+        constexpr int ch = decltype(cc_)::value;
+        if constexpr (S::y_pack(ch) == i) pack_item(nxt, ch);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (any) {
+      fence_acc1(acc);
+      rescale(m_old);
+    }
+    // this wave's loads of K j+2 and V j+1 have landed; the barrier publishes every wave's
+    // part and retires kslot(j+1) and vslot(j)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // ---- last tile: finish key half 1 and multiply (no next tile) ----------------------------
+  auto last = [&](auto cur, int j) {
+    const uint8_t* Vs = vslot(j);
+#pragma unroll
+    for (int v = 16; v < 32; ++v) exp_item(cur, v, true);
+#pragma unroll
+    for (int v = 16; v < 32; ++v) sum_item(cur, v);
+    pack_item(cur, 2);
+    pack_item(cur, 3);
+    fold();
+    // the products below read P right after the VALU wrote it
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p[2]), "+v"(p[3]));
+#pragma unroll
+    for (int g = 0; g < NY; ++g) mfma_o(acc[g % nD], v_frag(Vs, g), p[g / nD]);
+  };
+
+  // ---- prologue: tile 0's scores, max and key half 0 -------------------------------------
+  ld.issue_all(kslot(0), Kr, 0, T);
+  ld.issue_all(vslot(0), Vr, 0, T);
+  if (ntiles > 1) ld.issue_all(kslot(1), Kr, kBlockN, T);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  {
+    const uint8_t* K0 = kslot(0);
+#pragma unroll
+    for (int f = 0; f < NX; ++f) {
+      const bf16x8 a = k_frag(K0, f);
+      const int kb = f / nK, kk = f % nK;
+      f32x16& dst = kb ? s1a : s0;
+      if (kk == 0) mfma_s_first(dst, a, qf[kk]);
+      else mfma_s(dst, a, qf[kk]);
+    }
+    fence1(s0);
+    fence1(s1a);
+    const bool masked = nfull == 0;
+    const int lim = tile_lim(0);
+    pm[0] = pm[1] = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) max_item(Par<0>{}, u >> 3, u & 7, masked, lim);
+    // a row that sees no key of tile 0 keeps -inf here; its exponentials are all masked to 0
+    m_ref = halves_max1(fmaxf(pm[0], pm[1]));
+    mc = m_ref * c;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) exp_item(Par<0>{}, v, masked);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum_item(Par<0>{}, v);
+    pack_item(Par<0>{}, 0);
+    pack_item(Par<0>{}, 1);
+  }
+  // every wave is done with kslot(0) before iteration 0 refills it
+  __syncthreads();
+
+  int j = 0;
+  for (; j + 2 < nfull; j += 2) {
+    iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
+    iteration(Par<1>{}, Par<0>{}, j + 1, Flag<false>{}, IC<1>{});
+  }
+  // one more unmasked iteration when tile j + 1 needs no mask, after which tile j + 1's key
+  // half 1 moves to the even buffer the masked tail expects
+  if (j + 1 < nfull) {
+    iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
+    s1a = s1b;
+    ++j;
+  }
+  // masked tail (at most the diagonal tiles): one body, the next tile's key half 1 moved into
+  // the even buffer after each iteration so the roles never alternate
+  for (; j + 1 < ntiles; ++j) {
+    iteration(Par<0>{}, Par<1>{}, j, Flag<true>{}, IC<-1>{});
+    s1a = s1b;
+  }
+  last(Par<0>{}, j);
+
+  fence_acc1(acc);
+  const float l_half = lp[0] + lp[1];
+  const float r_half = rp[0] + rp[1];
+  const float l_tot = l_half + swap_halves(l_half);
+  const float r_tot = r_half + swap_halves(r_half);
+  if (qrow < Tq) {
+    // a row that sees no key at all (causal, fewer keys than queries) gets O = 0, LSE = -inf
+    const float inv = r_tot > 0.f ? 1.0f / r_tot : 0.f;
+    uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
+#pragma unroll
+    for (int db = 0; db < nD; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * h;
+        u32x2 w = {pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                   pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+    }
+    if (h == 0) Lh[qrow] = l_tot > 0.f ? (m_ref * c + log2_fast(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdBf16Problem& p) {
+  FwdKArgs k{};
+  k.q = static_cast<const uint16_t*>(p.q);
+  k.k = static_cast<const uint16_t*>(p.k);
+  k.v = static_cast<const uint16_t*>(p.v);
+  k.o = static_cast<uint16_t*>(p.o);
+  k.lse = p.lse;
+  k.cu_q = p.cu_q;
+  k.cu_k = p.cu_k;
+  k.G = p.Hq / p.Hkv;
+  k.hpw_log2 = k.G % 4 == 0 ? 2 : (k.G % 2 == 0 ? 1 : 0);
+  k.HG = p.Hq >> k.hpw_log2;
+  k.nbhg = p.B * k.HG;
+  k.nq = (p.max_q + (kBlockM >> k.hpw_log2) - 1) / (kBlockM >> k.hpw_log2);
+  k.Tq = p.Tq;
+  k.Tk = p.Tk;
+  if (p.cu_q) {   // packed (rows, heads, D)
+    k.q_rs = p.Hq * D;
+    k.kv_rs = p.Hkv * D;
+    k.q_bs = k.kv_bs = 0;
+    k.q_hs = D;
+    k.kv_hs = D;
+    k.lse_bs = 0;
+    k.lse_hs = p.Tq;
+  } else {        // (B, heads, rows, D)
+    k.q_rs = k.kv_rs = D;
+    k.q_hs = (int64_t)p.Tq * D;
+    k.kv_hs = (int64_t)p.Tk * D;
+    k.q_bs = (int64_t)p.Hq * k.q_hs;
+    k.kv_bs = (int64_t)p.Hkv * k.kv_hs;
+    k.lse_hs = p.Tq;
+    k.lse_bs = (int64_t)p.Hq * p.Tq;
+  }
+  k.c = p.scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL((fwd_q32_kernel<D, CAUSAL>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_q32(const FwdBf16Problem& p) {
+  if (p.D == 64) return p.causal ? launch<64, true>(p) : launch<64, false>(p);
+  return p.causal ? launch<128, true>(p) : launch<128, false>(p);
+}
+
+}  // namespace fa
