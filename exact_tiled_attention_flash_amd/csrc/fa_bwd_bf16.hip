@@ -18,7 +18,8 @@
 //                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
 //                    read of the row-major K tile.
-// Tiles reach LDS by direct HBM -> LDS loads (no staging registers), double-buffered; the
+// Tiles reach LDS by direct buffer -> LDS loads (no staging registers; rows past T arrive as
+// zeros), double-buffered and written as inline asm the compiler does not track; the
 // accumulator layout of S / S^T doubles as the B-operand layout of the following product
 // (k-slots permuted the same way for both operands), so P and dS never leave registers.
 
@@ -78,10 +79,11 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* __restrict__ dst, cons
   }
 }
 
-// 64 fp32 values of rows [row0, row0 + 64) (clamped to T - 1) straight into LDS; one wave.
-__device__ __forceinline__ void issue_stats(uint8_t* dst, const float* __restrict__ src, int row0,
-                                            int T, int lane) {
-  __builtin_amdgcn_global_load_lds(src + min(row0 + lane, T - 1), (lds_void*)dst, 4, 0, 0);
+// 64 fp32 values of rows [row0, row0 + 64) straight into LDS (rows at or past T: zeros); one
+// wave. rsrc covers the T values of one (b, h).
+__device__ __forceinline__ void issue_stats(uint8_t* dst, const i32x4& rsrc, int row0, int T,
+                                            int lane) {
+  buf_lds_dma<4>(dst, rsrc, (uint32_t)lane * 4u, (uint32_t)min(row0, T) * 4u);
 }
 
 // ------------------------------------------------------------------ dK, dV
@@ -140,13 +142,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int nqt = (T + kQTile - 1) / kQTile;
   const int qt0 = CAUSAL ? k0 / kQTile : 0;
 
-  const TileLoader<D> ld(wave, lane);
+  // The tile loads are untracked inline asm (see buf_lds_dma): the wait + barrier closing each
+  // iteration retires them before the stage is read, and retires the stage's readers before
+  // it is refilled.
+  const BufTileLoader<D> ld(wave, lane);
+  const uint32_t tbytes = (uint32_t)T * (uint32_t)D * 2u;
+  const i32x4 Qr = rows_rsrc(Q + base, tbytes), dOr = rows_rsrc(dO + base, tbytes);
+  const i32x4 Lr = rows_rsrc(L2 + rbase, (uint32_t)T * 4u), Dr = rows_rsrc(Dv + rbase, (uint32_t)T * 4u);
   auto fetch = [&](int qt, uint8_t* st) {
     const int q0 = qt * kQTile;
-    ld.issue_all(st + St::q, Q + base, q0, T);
-    ld.issue_all(st + St::dO, dO + base, q0, T);
-    if (wave == 0) issue_stats(st + St::lse2, L2 + rbase, q0, T, lane);
-    if (wave == 1) issue_stats(st + St::dvec, Dv + rbase, q0, T, lane);
+    ld.issue_all(st + St::q, Qr, q0, T);
+    ld.issue_all(st + St::dO, dOr, q0, T);
+    if (wave == 0) issue_stats(st + St::lse2, Lr, q0, T, lane);
+    if (wave == 1) issue_stats(st + St::dvec, Dr, q0, T, lane);
   };
 
   fetch(qt0, smem);
@@ -261,10 +269,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(T, q0 + kQueriesPerWG) : T;
   const int ntiles = (kend + kKTile - 1) / kKTile;
 
-  const TileLoader<D> ld(wave, lane);
+  // untracked tile loads, retired by the wait + barrier closing each iteration
+  const BufTileLoader<D> ld(wave, lane);
+  const uint32_t tbytes = (uint32_t)T * (uint32_t)D * 2u;
+  const i32x4 Kr = rows_rsrc(K + base, tbytes), Vr = rows_rsrc(V + base, tbytes);
   auto fetch = [&](int j, uint8_t* st) {
-    ld.issue_all(st, K + base, j * kKTile, T);
-    ld.issue_all(st + Tl::bytes, V + base, j * kKTile, T);
+    ld.issue_all(st, Kr, j * kKTile, T);
+    ld.issue_all(st + Tl::bytes, Vr, j * kKTile, T);
   };
   fetch(0, smem);
   __builtin_amdgcn_s_waitcnt(0);
