@@ -176,11 +176,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const int qb0 = q0 + qb * 32;
       if (CAUSAL && qb0 + 31 < kw0) continue;  // every query of the block precedes every key
       f32x16 s = f32x16{}, dp = f32x16{};
+      // operand fragments are read two k-steps ahead of their products (left to itself the
+      // compiler reads each one just before its product and waits out the LDS latency)
+      bf16x8 qa[nK], da[nK];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        qa[kk] = row_operand<D>(Qs, qb * 32 + l32, 2 * kk + h);
+        da[kk] = row_operand<D>(dOs, qb * 32 + l32, 2 * kk + h);
+      }
 #pragma unroll
       for (int kk = 0; kk < nK; ++kk) {
-        s = mfma32(row_operand<D>(Qs, qb * 32 + l32, 2 * kk + h), kf[kk], s);
-        dp = mfma32(row_operand<D>(dOs, qb * 32 + l32, 2 * kk + h), vf[kk], dp);
+        if (kk + 2 < nK) {
+          qa[kk + 2] = row_operand<D>(Qs, qb * 32 + l32, 2 * (kk + 2) + h);
+          da[kk + 2] = row_operand<D>(dOs, qb * 32 + l32, 2 * (kk + 2) + h);
+        }
+        s = mfma32(qa[kk], kf[kk], s);
+        dp = mfma32(da[kk], vf[kk], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // the first transposed operands of dV and dK load under the softmax work below
+      constexpr int nT = 2 * nD;   // products per tensor: (db, cc), cc fastest
+      bf16x8 ta[nT], tb[nT];
+      ta[0] = tr_operand<D>(dOs, 0, qb * 32, lane);
+      tb[0] = tr_operand<D>(Qs, 0, qb * 32, lane);
       // lane = key; register r = query qb0 + 8*(r/4) + 4h + (r%4)
       const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > T);
       f32x16 p, ds;
@@ -204,12 +222,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 8)};
       const bf16x8 dsb[2] = {pack8(ds, 0), pack8(ds, 8)};
 #pragma unroll
-      for (int db = 0; db < nD; ++db) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          dv[db] = mfma32(tr_operand<D>(dOs, db, qb * 32 + 16 * cc, lane), pb[cc], dv[db]);
-          dk[db] = mfma32(tr_operand<D>(Qs, db, qb * 32 + 16 * cc, lane), dsb[cc], dk[db]);
+      for (int t = 0; t < nT; ++t) {
+        const int db = t / 2, cc = t % 2;
+        if (t + 1 < nT) {
+          ta[t + 1] = tr_operand<D>(dOs, (t + 1) / 2, qb * 32 + 16 * ((t + 1) % 2), lane);
+          tb[t + 1] = tr_operand<D>(Qs, (t + 1) / 2, qb * 32 + 16 * ((t + 1) % 2), lane);
         }
+        dv[db] = mfma32(ta[t], pb[cc], dv[db]);
+        dk[db] = mfma32(tb[t], dsb[cc], dk[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -288,16 +309,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const uint8_t* Vs = Ks + Tl::bytes;
     if (!(CAUSAL && k0 > qw0 + 31)) {
       f32x16 s[2], dp[2];
+      // operand fragments are read two products ahead (f = nK kb + kk)
+      constexpr int nF = 2 * nK;
+      bf16x8 ka[nF], va[nF];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < nK; ++kk) {
-          s[kb] = mfma32(row_operand<D>(Ks, kb * 32 + l32, 2 * kk + h), qf[kk], s[kb]);
-          dp[kb] = mfma32(row_operand<D>(Vs, kb * 32 + l32, 2 * kk + h), dof[kk], dp[kb]);
-        }
+      for (int f = 0; f < 2; ++f) {
+        ka[f] = row_operand<D>(Ks, (f / nK) * 32 + l32, 2 * (f % nK) + h);
+        va[f] = row_operand<D>(Vs, (f / nK) * 32 + l32, 2 * (f % nK) + h);
       }
+#pragma unroll
+      for (int f = 0; f < nF; ++f) {
+        const int kb = f / nK, kk = f % nK;
+        if (f + 2 < nF) {
+          ka[f + 2] = row_operand<D>(Ks, ((f + 2) / nK) * 32 + l32, 2 * ((f + 2) % nK) + h);
+          va[f + 2] = row_operand<D>(Vs, ((f + 2) / nK) * 32 + l32, 2 * ((f + 2) % nK) + h);
+        }
+        if (kk == 0) {
+          s[kb] = f32x16{};
+          dp[kb] = f32x16{};
+        }
+        s[kb] = mfma32(ka[f], qf[kk], s[kb]);
+        dp[kb] = mfma32(va[f], dof[kk], dp[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the first transposed K operands load under the softmax work below
+      constexpr int nT = 4 * nD;   // (db, cc), cc fastest
+      bf16x8 ta[nT];
+      ta[0] = tr_operand<D>(Ks, 0, 0, lane);
+      ta[1] = tr_operand<D>(Ks, 0, 16, lane);
       // lane = query; register r of block kb = key k0 + 32 kb + 8*(r/4) + 4h + (r%4)
       const bool need_mask = (k0 + kKTile > T) || (CAUSAL && (k0 + kKTile - 1 > qw0));
       bf16x8 dsb[4];
@@ -318,10 +357,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         dsb[2 * kb + 1] = pack8(ds, 8);
       }
 #pragma unroll
-      for (int db = 0; db < nD; ++db) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-          dq[db] = mfma32(tr_operand<D>(Ks, db, 16 * cc, lane), dsb[cc], dq[db]);
+      for (int t = 0; t < nT; ++t) {
+        if (t + 2 < nT) ta[t + 2] = tr_operand<D>(Ks, (t + 2) / 4, 16 * ((t + 2) % 4), lane);
+        dq[t / 4] = mfma32(ta[t], dsb[t % 4], dq[t / 4]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
