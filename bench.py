@@ -83,7 +83,7 @@ COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_b4h16t4096d128_causal_traffic.json")
 # the sources the headline forward kernel is compiled from
 FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc", f)
-               for f in ("fa_fwd_bf16_q32.hip", "fa_fwd_parts.h", "fa_swz.h", "fa_common.h")]
+               for f in ("fa_fwd_bf16.hip", "fa_fwd_parts.h", "fa_swz.h", "fa_common.h")]
 
 
 def fwd_source_digest():

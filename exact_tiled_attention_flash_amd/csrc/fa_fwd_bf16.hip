@@ -1,48 +1,52 @@
-// Attention forward, bf16 storage, fp32 accumulation: hand-written gfx950 kernel with two
-// 32-query blocks per wave and one wave per SIMD. It runs the E4M3 Q K^T variant; with bf16 Q
-// and K the forward runs fwd_q32_kernel (one block per wave, two workgroups per compute unit),
-// which has the same arithmetic, and the QK8 = false code below is not instantiated.
+// Attention forward, bf16 storage (or E4M3 Q and K), fp32 accumulation: hand-written gfx950
+// kernel with one 32-query block per wave and two workgroups on every compute unit.
 //
 // Method: "Lab 06 - Attention kernels", section 3 (per query tile keep the row max m, row
 // sum l and accumulator acc; per key tile rescale by exp(m - m') and add exp(S - m') V;
 // finish with O = acc / l and LSE = m + log l; causal tiles above the diagonal are never
 // loaded, diagonal tiles are masked element-wise) and section 5 (one program per
-// (query tile, batch*head)). "Triton FlashAttention-2 forward", "The kernel" (queries
-// outermost, P rounded to the input dtype before the P V product, masked loads read zeros
-// beyond T). Section 2 of the lab page: subtracting any constant from the exponents and
-// dividing it back out is exact, which the lazy reference below relies on.
+// (query tile, batch*head)). "Triton FlashAttention-2 forward", "The kernel" (P rounded to
+// the input dtype before the P V product, masked loads read zeros beyond T). Section 2 of
+// the lab page: subtracting any constant from the exponents and dividing it back out is
+// exact, which the lazy reference relies on. The E4M3 Q K^T variant follows the same page's
+// "Stretch" list; the format and block scaling are described with the quantizer.
 //
 // gfx950 mapping
-//   * Workgroup: 256 threads = 4 waves, one per SIMD; 256 queries of one (b, h), 64 per
-//     wave as two 32-query blocks. Every K / V operand read from LDS feeds two
-//     matrix-core products (one per query block), which halves LDS traffic per flop
-//     compared with 32 queries per wave.
-//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one query per lane: a row's 64 scores of
-//     a tile sit in 32 registers of lane l and 32 of lane l ^ 32. The S^T accumulator
-//     layout is the B-operand layout of O^T += V^T P^T, so P never leaves registers; the
-//     V^T A operand is a transposing LDS read (ds_read_b64_tr_b16) of the row-major tile.
+//   * A wave issues a 32x32x16 product in about 12 cycles of its own time and the product
+//     occupies the matrix core for 32, so a single wave per SIMD leaves the matrix core idle
+//     while it works through the softmax. Every wave here holds one block of 32 queries (O^T
+//     in 64 AGPRs, Q^T in 32), a wave needs at most 256 registers, and two workgroups of 4
+//     waves share each compute unit: the SIMD runs one wave's products while the other
+//     wave's vector instructions issue.
+//   * Workgroup: 4 waves, 128 queries of one (b, h) (or 128 / hpw queries of hpw heads that
+//     share a K/V head, so every K/V tile loaded serves all of them). Causal grid order is
+//     heaviest query tile first; consecutive workgroup ids walk (b, head group) fastest,
+//     which keeps a head's tiles on one XCD (workgroups are dealt to the 8 XCDs round-robin)
+//     so its K and V are shared through that XCD's L2.
 //   * K and V tiles (64 keys) reach LDS by direct buffer -> LDS loads into XOR-swizzled
-//     row-major tiles, two slots each; K runs one tile ahead of V (see the pipeline). The
+//     row-major tiles, two slots each (64 KB a workgroup); K runs one tile ahead of V. The
 //     buffer resource ends at the last key row, so rows past it arrive as zeros and a load
-//     costs no vector arithmetic. The loads are inline asm, out of the compiler's sight:
-//     it would otherwise wait for every outstanding LDS read wherever it needs one of them.
+//     costs no vector arithmetic. The loads are inline asm, out of the compiler's sight: it
+//     would otherwise wait for every outstanding LDS read wherever it needs one of them.
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 for E4M3)
+//     puts one query per lane; a row's 64 scores of a tile sit in two 16-register blocks
+//     (key halves kb = 0, 1) of lanes l and l ^ 32. The S^T accumulator layout is the
+//     B-operand layout of O^T += V^T P^T, so P never leaves registers; the V^T A operand is
+//     a transposing LDS read (ds_read_b64_tr_b16) of the row-major tile.
 //   * exp(x) is exp2(x * scale * log2 e): one FMA and one v_exp_f32.
 //   * Lazy reference: a row's reference max m_ref moves only when a tile max exceeds it by
 //     more than 2^8 in the exp2 domain (and on the first tile), so P <= 2^8 and the O^T
 //     accumulators are rescaled in a rare wave-uniform branch, never in the steady state.
 //     O is normalised by the sum of the bf16-rounded P that actually multiplied V, so a
-//     dominant key's rounding cancels between numerator and denominator; LSE uses the
-//     fp32 sum of the unrounded exponentials.
-//   * Software pipeline across key tiles, one wave: phase X of iteration j runs the S
-//     products of tile j+1 on the matrix cores while the VALU finishes tile j (the last
-//     exponentials, fp32 and rounded row sums, bf16 packing); phase Y runs tile j's
-//     P V products while the VALU takes tile j+1's row max, moves the references and
-//     starts its exponentials. Each step of a phase holds one matrix-core product and a
-//     fixed share of the VALU work, fenced with sched_barrier so the compiler keeps the
-//     interleaving.
-//   * Causal grid order is heaviest query tile first; consecutive workgroup ids walk
-//     (b, h) fastest, which keeps all tiles of one head on one XCD (workgroups are dealt
-//     to the 8 XCDs round-robin) so K and V of a head are shared through that XCD's L2.
+//     dominant key's rounding cancels between numerator and denominator; LSE uses the fp32
+//     sum of the unrounded exponentials.
+//   * Software pipeline across key tiles: phase X of iteration j runs the S products of tile
+//     j+1 while the VALU finishes key half 1 of tile j (exponentials, fp32 and rounded sums,
+//     packing) and takes the max over key half 0 of tile j+1; phase Y runs tile j's P V
+//     products while the VALU takes the max over key half 1 of tile j+1, moves the
+//     references and works through key half 0 of tile j+1. Each step of a phase holds one
+//     product followed by a fixed share of the VALU work, fenced with sched_barrier. The
+//     E4M3 products (4 a tile for D = 128) sit on every fourth step of the same schedule.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -55,144 +59,64 @@ namespace {
 using namespace fwd;
 
 constexpr int kThreads = 256;
-constexpr int kBlockM = 256;   // queries per workgroup
+constexpr int kBlockM = 128;   // queries per workgroup, 32 per wave
 
-// E4M3 variant of the S products: 32 x 32 x 64 with a power-of-two scale per 32 k-values.
-// Lane l supplies row (A) / column (B) l % 32; its bytes 0-15 are k-values 16 (l / 32) + 0..15
-// of the first 32-value block and bytes 16-31 the same positions of the second block; the
-// scale of block q of a row comes from lane row + 32 q, byte BYTE of its scale register
-// (op_sel carries bit 0 of BYTE, op_sel_hi bit 1).
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-template <bool FIRST, int BYTE>
-__device__ __forceinline__ void mfma8_s(f32x16& d, const i32x8& a, const i32x8& b, uint32_t sa,
-                                        uint32_t sb) {
-  static_assert(BYTE == 0 || BYTE == 2, "scale byte");
-  if constexpr (FIRST && BYTE == 0)
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4"
-                 : "=&v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
-  else if constexpr (FIRST)
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[1,1,0]"
-                 : "=&v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
-  else if constexpr (BYTE == 0)
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4"
-                 : "+v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
-  else
-    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,1,0]"
-                 : "+v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+// 20 wait states between the last product writing x and any later instruction that uses it.
+__device__ __forceinline__ void fence1(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x));
 }
 
-// A [64 x D] E4M3 tile in LDS (D bytes a row, 16-byte chunks XOR-swizzled so that 8 (D = 128)
-// or 4 (D = 64) consecutive rows reading one logical chunk hit distinct banks for 32 and for
-// 64 banks), followed by its block-scale bytes: D / 32 per row, in one dword per row (a direct
-// HBM -> LDS load of 1 or 2 bytes a lane writes a zero-extended dword a lane).
-template <int D>
-struct SwzTile8 {
-  static constexpr int CH = D / 16;
-  static constexpr int RB = D;
-  static constexpr int SB = D / 32;     // scale bytes per row in HBM
-  static constexpr int sc_offset = 64 * RB;
-  static constexpr int loadsPerWave = 64 * CH / 256;
-  __device__ static __forceinline__ int swz(int row) { return D == 128 ? (row & 7) : ((row >> 1) & 3); }
-  __device__ static __forceinline__ int offset(int row, int lchunk) {
-    return row * RB + ((lchunk ^ swz(row)) << 4);
-  }
-};
-
-// Direct HBM -> LDS loads of a 64-row E4M3 tile and its scales by the 4 waves of a workgroup
-// (the same lane-to-chunk rule as TileLoader); wave 0 also moves the 64 rows' scale bytes.
-template <int D>
-struct TileLoader8 {
-  using Tl = SwzTile8<D>;
-  uint32_t vofs[Tl::loadsPerWave];   // byte offset of the lane's i-th chunk from the tile's row 0
-  int wave, lane;
-  uint32_t rsb, srs;   // bytes between rows of the codes and of the scales
-  __device__ __forceinline__ TileLoader8(int wave_, int lane_, int row_stride)
-      : wave(wave_), lane(lane_), rsb((uint32_t)row_stride), srs((uint32_t)row_stride / 32u) {
-#pragma unroll
-    for (int i = 0; i < Tl::loadsPerWave; ++i) {
-      const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
-      const int row = u / Tl::CH;
-      vofs[i] = (uint32_t)row * rsb + (uint32_t)(((u % Tl::CH) ^ Tl::swz(row)) * 16);
-    }
-  }
-  // codes and scales come through buffer resources over the T rows (rows at or past T: zeros)
-  __device__ __forceinline__ void issue(uint8_t* dst, const i32x4& rsrc, int row0, int T,
-                                        int i) const {
-    buf_lds_dma<16>(dst + (wave * Tl::loadsPerWave + i) * 1024, rsrc, vofs[i],
-                    (uint32_t)min(row0, T) * rsb);
-  }
-  __device__ __forceinline__ void issue_scales(uint8_t* dst, const i32x4& srsrc, int row0,
-                                               int T) const {
-    if (wave == 0)
-      buf_lds_dma<Tl::SB>(dst + Tl::sc_offset, srsrc, (uint32_t)lane * srs,
-                          (uint32_t)min(row0, T) * srs);
-  }
-  __device__ __forceinline__ void issue_all(uint8_t* dst, const i32x4& rsrc, const i32x4& srsrc,
-                                            int row0, int T) const {
-#pragma unroll
-    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, rsrc, row0, T, i);
-    issue_scales(dst, srsrc, row0, T);
-  }
-};
-
-
 // ---- per-step work assignment (all compile-time) --------------------------------------
-// Items of one tile: 64 score elements per lane, v = 32 qb + 16 kb + r; 8 chunks of 8
-// (v / 8 = 4 qb + cc, the B operand P[qb][cc]); 16 max items per key half (pairs of
-// elements). Query block 0 of a tile is finished in phase Y of the iteration before it is
-// used, query block 1 in phase X of its own iteration.
-
+// Items of one tile: 32 score elements per lane, v = 16 kb + r; 4 chunks of 8 (v / 8 = ch,
+// the B operand P[ch] of keys 16 ch .. 16 ch + 15); 8 max items per key half (pairs of
+// elements). Key half 0 of a tile is finished in phase Y of the iteration before the one
+// that multiplies it, key half 1 in phase X of that iteration.
 template <int D>
-struct Sched {
+struct Sched1 {
   static constexpr int nK = D / 16, nD = D / 32;
-  static constexpr int NX = 4 * nK;                  // phase X steps (S products)
-  static constexpr int NY = 8 * nD;                  // phase Y steps (P V products)
-  // phase Y: max over key half kb = 1, reference update, then query block 0's
-  // exponentials, sums and packing
-  static constexpr int YM0 = 2, YM1 = 2 + NY / 4, YR = YM1, YE0 = YR + 1, YE1 = NY - NY / 8;
+  static constexpr int NX = 2 * nK;   // phase X steps (S products, f = nK kb + kk)
+  static constexpr int NY = 4 * nD;   // phase Y steps (P V products, g = nD cc + db)
+  static constexpr int XE0 = 0, XE1 = NX - 4, XS0 = 1, XS1 = NX - 2;
+  static constexpr int XM0 = nK + 2, XM1 = NX;
+  static constexpr int YM0 = 2, YM1 = 2 + NY / 8, YR = YM1, YE0 = YR + 1, YE1 = NY - 2;
   static constexpr int YS0 = YE0 + 1, YS1 = NY;
-  // phase X: query block 1's exponentials, sums and packing, then the fold of the tile's
-  // sums; max over key half kb = 0 of the next tile once its products are done
-  static constexpr int XE0 = 0, XE1 = NX / 2, XS0 = 1, XS1 = NX / 2 + 4;
-  static constexpr int XM0 = NX / 2 + 2, XM1 = NX;
-  static constexpr int y_exp(int v) { return win_step(v, 32, YE0, YE1); }
-  static constexpr int y_sum(int v) { return win_step(v, 32, YS0, YS1); }
-  static constexpr int x_exp(int v) { return win_step(v - 32, 32, XE0, XE1); }
-  static constexpr int x_sum(int v) { return win_step(v - 32, 32, XS0, XS1); }
-  // a chunk is packed one step after its last exponential
-  static constexpr int y_pack(int ch) { return y_exp(8 * ch + 7) + 1; }
-  static constexpr int x_pack(int ch) { return x_exp(8 * ch + 7) + 1; }
-  static constexpr int XF = (x_sum(63) > x_pack(7) ? x_sum(63) : x_pack(7)) + 1;
-  static constexpr int x_max(int u) { return win_step(u, 16, XM0, XM1); }   // kb = 0
-  static constexpr int y_max(int u) { return win_step(u, 16, YM0, YM1); }   // kb = 1
-  // every sum and pack comes after the exponentials it reads, within its phase
+  static constexpr int x_exp(int v) { return win_step(v - 16, 16, XE0, XE1); }   // v in [16, 32)
+  static constexpr int x_sum(int v) { return win_step(v - 16, 16, XS0, XS1); }
+  static constexpr int x_pack(int ch) { return x_exp(8 * ch + 7) + 1; }            // ch = 2, 3
+  static constexpr int XF = (x_sum(31) > x_pack(3) ? x_sum(31) : x_pack(3)) + 1;
+  static constexpr int x_max(int t) { return win_step(t, 8, XM0, XM1); }           // kb = 0
+  static constexpr int y_max(int t) { return win_step(t, 8, YM0, YM1); }           // kb = 1
+  static constexpr int y_exp(int v) { return win_step(v, 16, YE0, YE1); }          // v in [0, 16)
+  static constexpr int y_sum(int v) { return win_step(v, 16, YS0, YS1); }
+  // chunk ch (0, 1) of the next tile overwrites P[ch] one step after this tile's last product
+  // that reads it (steps nD ch .. nD ch + nD - 1)
+  static constexpr int y_pack(int ch) {
+    return y_exp(8 * ch + 7) + 1 > nD * (ch + 1) + 1 ? y_exp(8 * ch + 7) + 1 : nD * (ch + 1) + 1;
+  }
   static constexpr bool valid() {
-    for (int v = 0; v < 32; ++v)
-      if (y_sum(v) <= y_exp(v) || y_sum(v) >= NY || y_pack(v / 8) >= NY) return false;
-    for (int v = 32; v < 64; ++v)
+    for (int v = 0; v < 16; ++v)
+      if (y_sum(v) <= y_exp(v) || y_sum(v) >= NY) return false;
+    for (int v = 16; v < 32; ++v)
       if (x_sum(v) <= x_exp(v) || x_sum(v) >= NX) return false;
-    return YR < YE0 && XE1 <= NX && XF < NX && y_max(15) < YR;
+    return YR < YE0 && XF < NX && y_max(7) < YR && y_pack(1) < NY && x_pack(3) < NX &&
+           XM0 > nK && x_max(7) < NX;
   }
 };
-static_assert(Sched<128>::valid() && Sched<64>::valid(), "pipeline schedule order");
-
+static_assert(Sched1<128>::valid() && Sched1<64>::valid(), "pipeline schedule order");
 
 template <int D, bool CAUSAL, bool QK8>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs args) {
+__global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs args) {
   using Tl = SwzTile<D>;
-  using S = Sched<D>;
-  constexpr int nD = D / 32;   // 32-row blocks of O^T
-  constexpr int nK = D / 16;   // k-steps of S^T
-  constexpr int nKF = 2 * nK;  // K operand fragments per tile: f = nK kb + kk
-  constexpr int nVF = 4 * nD;  // V operand fragments per tile: g = nD cc + db
   using Tl8 = SwzTile8<D>;
-  constexpr int nK8 = D / 64;    // k-steps of an E4M3 S product
-  constexpr int nKF8 = 2 * nK8;  // E4M3 K fragments per tile: f = nK8 kb + kk
+  using S = Sched1<D>;
+  constexpr int nD = D / 32;      // 32-row blocks of O^T
+  constexpr int nK = D / 16;      // k-steps of S^T = K Q^T (bf16)
+  constexpr int nK8 = D / 64;     // k-steps of the E4M3 products
+  constexpr int nKF8 = 2 * nK8;   // E4M3 K fragments per tile: f = nK8 kb + kk
+  constexpr int NX = S::NX, NY = S::NY;
   // odd steps of phase X that issue K loads (E4M3: the codes, then one for the scales)
   constexpr int LK = QK8 ? Tl8::loadsPerWave + 1 : Tl::loadsPerWave;
-  // Two slots per tensor, each its own LDS object: where the slot parity is known at compile
-  // time the compiler can tell a slot being refilled by DMA from the one being read, and
-  // need not wait for the DMA before every LDS read.
+  static_assert(LK + Tl::loadsPerWave <= NX / 2, "tile loads fit the odd steps of phase X");
   __shared__ __attribute__((aligned(1024))) uint8_t ks0[Tl::bytes], ks1[Tl::bytes];
   __shared__ __attribute__((aligned(1024))) uint8_t vs0[Tl::bytes], vs1[Tl::bytes];
 
@@ -204,8 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
 
   const float c = args.c;
   // Workgroup -> (query tile, batch, head group): heaviest causal tiles first, (batch, head
-  // group) fastest. A workgroup serves hpw query heads that share one K/V head, each with
-  // 256 / hpw consecutive queries (64 per wave), so every K/V tile it loads feeds all of them.
+  // group) fastest. hpw query heads sharing one K/V head, 128 / hpw consecutive queries each.
   const int L = workgroup_id();
   const int r = L % args.nbhg;
   int qt = L / args.nbhg;
@@ -213,10 +136,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
   const int b = r / args.HG, hg = r % args.HG;
   const int hpw = 1 << args.hpw_log2;
   const int h0 = hg * hpw;
-  const int hq = h0 + (wave & (hpw - 1));             // this wave's query head
-  const int kvh = h0 / args.G;                            // the workgroup's K/V head
-  const int qrows = kBlockM >> args.hpw_log2;             // queries per head in this workgroup
-  // sequence bounds (packed batches: clamped into the arrays whatever the offsets hold)
+  const int hq = h0 + (wave & (hpw - 1));   // this wave's query head
+  const int kvh = h0 / args.G;
+  const int qrows = kBlockM >> args.hpw_log2;
   int qs = 0, Tq = args.Tq, ks = 0, Tk = args.Tk;
   if (args.cu_q) {
     qs = min(max(args.cu_q[b], 0), args.Tq);
@@ -229,19 +151,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     Tk = __builtin_amdgcn_readfirstlane(Tk);
   }
   const int q0 = qt * qrows;
-  if (q0 >= Tq) return;   // past this sequence's queries (packed batches); uniform per workgroup
-  const int qw0 = q0 + (wave >> args.hpw_log2) * 64;
-  const int shift = CAUSAL ? Tk - Tq : 0;   // bottom-right alignment: 0 when Tq == Tk
+  if (q0 >= Tq) return;   // uniform per workgroup
+  const int qw0 = q0 + (wave >> args.hpw_log2) * 32;   // this wave's first query
+  const int shift = CAUSAL ? Tk - Tq : 0;              // bottom-right alignment
+  const int qrow = qw0 + l32;                          // this lane's query
 
   const uint16_t* Qh = args.q + b * args.q_bs + (int64_t)qs * args.q_rs + hq * args.q_hs;
   uint16_t* Oh = args.o + b * args.q_bs + (int64_t)qs * args.q_rs + hq * args.q_hs;
   float* Lh = args.lse + b * args.lse_bs + hq * args.lse_hs + qs;
   const uint16_t* Kh = args.k + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
   const uint16_t* Vh = args.v + b * args.kv_bs + (int64_t)ks * args.kv_rs + kvh * args.kv_hs;
-  const int T = Tk;   // key rows of this sequence (tile rows at or past T load as zeros)
+  const int T = Tk;
   auto kslot = [&](int t) -> uint8_t* { return (t & 1) ? ks1 : ks0; };
   auto vslot = [&](int t) -> uint8_t* { return (t & 1) ? vs1 : vs0; };
-  // jp: parity of j as IC<0> / IC<1>, or IC<-1> when only known at run time
   auto kslot_p = [&](auto jp, int j, int d) -> uint8_t* {
     constexpr int P = decltype(jp)::value;
     if constexpr (P < 0) return kslot(j + d);
@@ -264,234 +186,189 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     Ksr = rows_rsrc(args.ks + ko / 32, kv_bytes / 64u);
   }
 
-  // Q^T fragments stay in registers: query block qb, lane holds query qw0 + 32 qb + l32,
-  // d = 16 kk + 8 h + 0..7. E4M3: codes of k-step kk at d = 64 kk + 16 h + 0..15 and
-  // 64 kk + 32 + 16 h + 0..15, and the row's scale bytes shifted so that byte 2 kk is block
-  // 2 kk + h (the block whose scale this lane half supplies).
-  bf16x8 qf[2][QK8 ? 1 : nK];
-  i32x8 qf8[2][QK8 ? nK8 : 1];
-  uint32_t qsc[2] = {0u, 0u};
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = qw0 + 32 * qb + l32;
-    if constexpr (!QK8) {
-#pragma unroll
-      for (int kk = 0; kk < nK; ++kk) {
-        u32x4 x = qrow < Tq
-                      ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-        qf[qb][kk] = as_bf16x8(x);
-      }
-    } else {
-      const int64_t qe = b * args.q_bs + (int64_t)(qs + qrow) * args.q_rs + hq * args.q_hs;
-      const uint8_t* Qr = args.q8 + qe;
-#pragma unroll
-      for (int kk = 0; kk < nK8; ++kk) {
-        u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-        if (qrow < Tq) {
-          x0 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 16 * h);
-          x1 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 32 + 16 * h);
-        }
-        qf8[qb][kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                            (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      }
-      uint32_t sc = 0x7f7f7f7fu;
-      if (qrow < Tq) {
-        const uint8_t* Qs = args.qs + qe / 32;
-        sc = D == 128 ? *reinterpret_cast<const uint32_t*>(Qs) : *reinterpret_cast<const uint16_t*>(Qs);
-      }
-      qsc[qb] = sc >> (8 * h);
-    }
-  }
-  // Move Q^T into AGPRs now and pad the accumulator writes before any product reads them.
+  // Q^T fragments, moved into AGPRs: lane holds query qrow, d = 16 kk + 8 h + 0..7. E4M3: codes
+  // of k-step kk at d = 64 kk + 16 h + 0..15 and 64 kk + 32 + 16 h + 0..15, and the row's scale
+  // bytes shifted so that byte 2 kk is block 2 kk + h (the block whose scale this lane half
+  // supplies).
+  bf16x8 qf[QK8 ? 1 : nK];
+  i32x8 qf8[QK8 ? nK8 : 1];
+  uint32_t qsc = 0u;
   if constexpr (!QK8) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int kk = 0; kk < nK; ++kk) {
+      u32x4 x = qrow < Tq ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+      qf[kk] = as_bf16x8(x);
+    }
 #pragma unroll
-      for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
+    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[kk]));
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[qb][kk]));
+    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(qf[kk]));
   } else {
+    const int64_t qe = b * args.q_bs + (int64_t)(qs + qrow) * args.q_rs + hq * args.q_hs;
+    const uint8_t* Qr = args.q8 + qe;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int kk = 0; kk < nK8; ++kk) asm volatile("" : "+a"(qf8[qb][kk]));
-      asm volatile("" : "+v"(qsc[qb]));
+    for (int kk = 0; kk < nK8; ++kk) {
+      u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+      if (qrow < Tq) {
+        x0 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 16 * h);
+        x1 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 32 + 16 * h);
+      }
+      qf8[kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                      (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
     }
+    uint32_t sc = 0x7f7f7f7fu;
+    if (qrow < Tq) {
+      const uint8_t* Qs = args.qs + qe / 32;
+      sc = D == 128 ? *reinterpret_cast<const uint32_t*>(Qs) : *reinterpret_cast<const uint16_t*>(Qs);
+    }
+    qsc = sc >> (8 * h);
+#pragma unroll
+    for (int kk = 0; kk < nK8; ++kk) asm volatile("" : "+a"(qf8[kk]));
+    asm volatile("" : "+v"(qsc));
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int kk = 0; kk < nK8; ++kk) asm volatile("" : "+a"(qf8[qb][kk]));
-      asm volatile("" : "+v"(qsc[qb]));
-    }
+    for (int kk = 0; kk < nK8; ++kk) asm volatile("" : "+a"(qf8[kk]));
+    asm volatile("" : "+v"(qsc));
   }
 
   // keys seen by the workgroup's last query, and by all of its queries
   const int kend = CAUSAL ? min(Tk, q0 + qrows + shift) : Tk;
   const int ntiles = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
   const int kall = CAUSAL ? min(Tk, q0 + shift + 1) : Tk;
-  // tiles [0, nfull) need no mask for any query of this workgroup
   const int nfull = kall > 0 ? min(kall / kBlockN, ntiles) : 0;
 
-  if (ntiles == 0) {   // no query of this workgroup sees a key (uniform per workgroup)
+  if (ntiles == 0) {   // no query of this workgroup sees a key
+    if (qrow < Tq) {
+      uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qrow = qw0 + 32 * qb + l32;
-      if (qrow < Tq) {
-        uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
-#pragma unroll
-        for (int d0 = 0; d0 < D; d0 += 8)
-          if ((d0 / 8) % 2 == h) *reinterpret_cast<u32x4*>(orow + d0) = u32x4{0u, 0u, 0u, 0u};
-        if (h == 0) Lh[qrow] = kNegInf;
-      }
+      for (int d0 = 0; d0 < D; d0 += 8)
+        if ((d0 / 8) % 2 == h) *reinterpret_cast<u32x4*>(orow + d0) = u32x4{0u, 0u, 0u, 0u};
+      if (h == 0) Lh[qrow] = kNegInf;
     }
     return;
   }
 
-  f32x16 acc[2][nD];
+  f32x16 acc[nD];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < nD; ++db) acc[qb][db] = f32x16{};
-  float m_ref[2], mc[2];            // reference max (raw score units) and m_ref * c
-  // row sums per (qb, key half kb): fp32 exponentials (l) and bf16-rounded P (r), for the
-  // tiles already folded in (lp, rp) and for the tile in progress (tl, tr), which may
-  // already use a newer reference
-  float lp[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, rp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  float tl[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, tr[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  float pm[2][2];                   // partial row maxima of the next tile, per (qb, kb)
-  // Scores -> exponentials and the bf16 P of a tile, per query block. Query block 0 of a
-  // tile is finished in the iteration before the tile's own, so its buffers are free again
-  // when the next tile's products start: one score buffer for block 0, two for block 1
-  // (tile parity); P of block 0 is double-buffered, P of block 1 single.
-  f32x16 s0[2], s1a[2], s1b[2];
-  bf16x8 p0a[4], p0b[4], p1[4];
-  // buffers of a tile of parity par: score block (qb, kb), P operand (qb, cc)
-  auto sblk = [&](auto par, int qb, int kb) -> f32x16& {
-    if constexpr (decltype(par)::value == 0) return qb ? s1a[kb] : s0[kb];
-    else return qb ? s1b[kb] : s0[kb];
-  };
-  auto pop = [&](auto par, int qb, int cc) -> bf16x8& {
-    if constexpr (decltype(par)::value == 0) return qb ? p1[cc] : p0a[cc];
-    else return qb ? p1[cc] : p0b[cc];
+  for (int db = 0; db < nD; ++db) acc[db] = f32x16{};
+  float m_ref, mc;                  // reference max (raw score units) and m_ref * c
+  // row sums per key half: fp32 exponentials (l) and bf16-rounded P (r, two chains), for the
+  // tiles already folded in (lp, rp) and for the tile in progress (tl, tr)
+  float lp[2] = {0.f, 0.f}, rp[2] = {0.f, 0.f}, tl[2] = {0.f, 0.f}, tr[2] = {0.f, 0.f};
+  float pm[2];                      // partial row maxima of the next tile, per key half
+  // scores: key half 0 (one buffer) and key half 1 (two, by tile parity); P chunks 0-3
+  f32x16 s0, s1a, s1b;
+  bf16x8 p[4];
+  auto sblk = [&](auto par, int kb) -> f32x16& {
+    if constexpr (decltype(par)::value == 0) return kb ? s1a : s0;
+    else return kb ? s1b : s0;
   };
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  // element (kb, r) of a lane is key 32 kb + 8 (r / 4) + (r % 4) + 4 h of the tile; it is
-  // valid for query block qb iff that local index is below lim[qb]
-  auto tile_lim = [&](int t, int (&lim)[2]) {
+  // element r of key half kb is key 32 kb + 8 (r / 4) + (r % 4) + 4 h of the tile; it is
+  // valid iff that local index is below the returned limit
+  auto tile_lim = [&](int t) {
     const int k0 = t * kBlockN;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      int l = Tk - k0;
-      if (CAUSAL) l = min(l, qw0 + 32 * qb + l32 + shift - k0 + 1);
-      lim[qb] = l - 4 * h;
-    }
+    int l = Tk - k0;
+    if (CAUSAL) l = min(l, qrow + shift - k0 + 1);
+    return l - 4 * h;
   };
 
   // ---- work items ------------------------------------------------------------------------
-  auto max_item = [&](auto par, int qb, int kb, int t, bool masked, const int (&lim)[2]) {
-    f32x16& x = sblk(par, qb, kb);
-    float a = x[2 * t], b = x[2 * t + 1];
+  auto max_item = [&](auto par, int kb, int t, bool masked, int lim) {
+    f32x16& x = sblk(par, kb);
+    float a = x[2 * t], b2 = x[2 * t + 1];
     if (masked) {
       const int kla = 32 * kb + 8 * (t >> 1) + 2 * (t & 1);
-      a = kla < lim[qb] ? a : kNegInf;
-      b = kla + 1 < lim[qb] ? b : kNegInf;
+      a = kla < lim ? a : kNegInf;
+      b2 = kla + 1 < lim ? b2 : kNegInf;
       x[2 * t] = a;
-      x[2 * t + 1] = b;
+      x[2 * t + 1] = b2;
     }
-    // one v_max3 per pair (left to itself the compiler reassociates the chain into a tree
-    // of twice as many instructions); the scores' producers are fenced before the first item
-    float m = pm[qb][kb];
-    asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b));
-    pm[qb][kb] = m;
+    float m = pm[kb];
+    asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b2));
+    pm[kb] = m;
   };
   auto exp_item = [&](auto par, int v, bool masked) {
-    const int qb = v >> 5, kb = (v >> 4) & 1, r = v & 15;
-    f32x16& blk = sblk(par, qb, kb);
-    const float x = blk[r];
-    const float e = exp2_fast(fmaf(x, c, -mc[qb]));
-    blk[r] = (masked && x == kNegInf) ? 0.f : e;
+    const int kb = v >> 4, rr = v & 15;
+    f32x16& blk = sblk(par, kb);
+    const float x = blk[rr];
+    float e = exp2_fast(fmaf(x, c, -mc));
+    e = (masked && x == kNegInf) ? 0.f : e;
+    asm volatile("" : "+v"(e));   // keeps the exponential at its step
+    blk[rr] = e;
   };
-  // The sums are pinned to their step with an empty asm that takes them as operands:
-  // otherwise the compiler sinks the whole chain of additions to the end of the iteration,
-  // where it runs as one block with no product to hide under.
   auto sum_item = [&](auto par, int v) {
-    const int qb = v >> 5, kb = (v >> 4) & 1, r = v & 15;
-    tl[qb][kb] += sblk(par, qb, kb)[r];
-    asm volatile("" : "+v"(tl[qb][kb]));
+    const int kb = v >> 4, rr = v & 15;
+    tl[kb] += sblk(par, kb)[rr];
+    asm volatile("" : "+v"(tl[kb]));
   };
-  // Pack chunk ch to the bf16 B operand and add the rounded values. The words are summed
-  // before they are gathered into the operand vector: with this toolchain,
-  // v_dot2c_f32_bf16 applied to an element of a 4-vector reads the vector's first register
-  // for the second element too.
-  auto pack_item = [&](auto spar, auto ppar, int ch) {
-    const int qb = ch >> 2, cc = ch & 3, kb = cc >> 1, o = (cc & 1) * 8;
-    const f32x16& sv = sblk(spar, qb, kb);
+  // pack chunk ch to the bf16 B operand P[ch] and add the rounded values
+  auto pack_item = [&](auto par, int ch) {
+    const int kb = ch >> 1, o = (ch & 1) * 8;
+    const f32x16& sv = sblk(par, kb);
     const uint32_t w0 = pack_bf16x2(sv[o + 0], sv[o + 1]), w1 = pack_bf16x2(sv[o + 2], sv[o + 3]);
     const uint32_t w2 = pack_bf16x2(sv[o + 4], sv[o + 5]), w3 = pack_bf16x2(sv[o + 6], sv[o + 7]);
-    tr[qb][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, tr[qb][0], false);
-    tr[qb][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tr[qb][1], false);
-    tr[qb][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, tr[qb][0], false);
-    tr[qb][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, tr[qb][1], false);
-    asm volatile("" : "+v"(tr[qb][0]), "+v"(tr[qb][1]));
-    pop(ppar, qb, cc) = as_bf16x8(u32x4{w0, w1, w2, w3});
+    tr[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, tr[0], false);
+    tr[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, tr[1], false);
+    tr[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, tr[0], false);
+    tr[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, tr[1], false);
+    asm volatile("" : "+v"(tr[0]), "+v"(tr[1]));
+    p[ch] = as_bf16x8(u32x4{w0, w1, w2, w3});
   };
-  // the finished tile's sums join the running sums (same reference by now)
   auto fold = [&]() {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        lp[qb][kb] += tl[qb][kb];
-        rp[qb][kb] += tr[qb][kb];
-        tl[qb][kb] = 0.f;
-        tr[qb][kb] = 0.f;
-      }
-  };
-  // Full-row maxima of the next tile; moves the references (all rows of the wave together,
-  // when any row exceeds its reference by more than the margin) and returns whether the
-  // folded sums and the accumulators need the rescale by exp(m_old - m_ref).
-  auto reduce = [&](float (&m_old)[2]) {
-    float a = fmaxf(pm[0][0], pm[0][1]), b = fmaxf(pm[1][0], pm[1][1]);
-    halves_max2(a, b, h);
-    // (a reference still at -inf belongs to a row that has not seen a key yet)
-    const bool need = (a - m_ref[0]) * c > kRescaleLog2 || (b - m_ref[1]) * c > kRescaleLog2 ||
-                      m_ref[0] == kNegInf || m_ref[1] == kNegInf;
-    const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-    m_old[0] = m_ref[0];
-    m_old[1] = m_ref[1];
-    m_ref[0] = any ? fmaxf(m_ref[0], a) : m_ref[0];
-    m_ref[1] = any ? fmaxf(m_ref[1], b) : m_ref[1];
-    mc[0] = m_ref[0] * c;
-    mc[1] = m_ref[1] * c;
-    return any;
-  };
-  auto rescale = [&](const float (&m_old)[2]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float alpha = m_old[qb] == m_ref[qb] ? 1.f : exp2_fast((m_old[qb] - m_ref[qb]) * c);
-#pragma unroll
-      for (int db = 0; db < nD; ++db) acc[qb][db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        lp[qb][kb] *= alpha;
-        rp[qb][kb] *= alpha;
-      }
+    for (int i = 0; i < 2; ++i) {
+      lp[i] += tl[i];
+      rp[i] += tr[i];
+      tl[i] = 0.f;
+      tr[i] = 0.f;
     }
   };
-  auto reset_max = [&]() {
+  // full-row max of the next tile; moves the references (every row of the wave, when any row
+  // exceeds its reference by more than the margin) and says whether a rescale is due
+  auto reduce = [&](float& m_old) {
+    const float a = halves_max1(fmaxf(pm[0], pm[1]));
+    const bool need = (a - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
+    const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+    m_old = m_ref;
+    m_ref = any ? fmaxf(m_ref, a) : m_ref;
+    mc = m_ref * c;
+    return any;
+  };
+  auto rescale = [&](float m_old) {
+    const float alpha = m_old == m_ref ? 1.f : exp2_fast((m_old - m_ref) * c);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) pm[qb][0] = pm[qb][1] = kNegInf;
+    for (int db = 0; db < nD; ++db) acc[db] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lp[i] *= alpha;
+      rp[i] *= alpha;
+    }
   };
+  // Operand reads from a tile: only the in-row part of an address depends on the lane and the
+  // k-step, so it is kept per k-step (koff) or per 32-column block of V (voff); the key-half
+  // and 16-key chunk steps (32 and 16 rows) leave the swizzle unchanged and become constant
+  // offsets. K fragment f = nK kb + kk: 8 bf16 of key row 32 kb + l32, logical chunk 2 kk + h.
+  // V^T fragment g = nD cc + db: as tr_operand with kbase = 16 cc.
+  uint32_t koff[nK], voff[nD][2];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) koff[kk] = (uint32_t)Tl::offset(l32, 2 * kk + h);
+  {
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int row = 4 * (g4 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < nD; ++db) {
+      const int d0 = db * 32 + (g4 & 1) * 16 + 4 * (i16 & 3);
+      voff[db][0] = (uint32_t)(Tl::offset(row, d0 >> 3) + (d0 & 7) * 2);
+      voff[db][1] = (uint32_t)(Tl::offset(row + 8, d0 >> 3) + (d0 & 7) * 2);
+    }
+  }
   auto k_frag = [&](const uint8_t* Ks, int f) {
-    return row_operand<D>(Ks, (f / nK) * 32 + l32, 2 * (f % nK) + h);
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (f / nK) * 32 * Tl::RB + koff[f % nK]));
   };
-  auto v_frag = [&](const uint8_t* Vs, int g) { return tr_operand<D>(Vs, g % nD, 16 * (g / nD), lane); };
   // E4M3 K fragment f = nK8 kb + kk: key row 32 kb + l32, the two 16-byte chunks of this lane
   // half in k-step kk; and the row's scale bytes, shifted like the Q scales
   auto k_frag8 = [&](const uint8_t* Ks, int f) {
@@ -505,21 +382,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     const uint32_t sc = *reinterpret_cast<const uint32_t*>(Ks + Tl8::sc_offset + (32 * kb + l32) * 4);
     return sc >> (8 * h);
   };
+  auto v_frag = [&](const uint8_t* Vs, int g) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint8_t* base = Vs + (g / nD) * 16 * Tl::RB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[g % nD][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + voff[g % nD][1]));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
 
   // ---- one pipelined iteration: tile j finishes, tile j+1 starts --------------------------
-  // On entry: query block 0 of tile j is exponentiated, summed (tl, tr) and packed (pc);
-  // cur holds query block 1's scores; tile j+1's K is in kslot(j+1), tile j's V in vslot(j).
-  // cur / nxt: parity tags of tile j and tile j+1
+  // On entry: key half 0 of tile j is exponentiated, summed and packed (P[0], P[1]); cur holds
+  // key half 1's scores; tile j+1's K is in kslot(j+1), tile j's V in vslot(j).
   auto iteration = [&](auto cur, auto nxt, int j, auto mask_tag, auto jp) {
-    constexpr bool MASK = decltype(mask_tag)::value;   // tile j or j+1 may need masks
-    int lim[2];
-    if (MASK) tile_lim(j + 1, lim);
+    constexpr bool MASK = decltype(mask_tag)::value;   // tile j+1 may need masks
+    const int lim = MASK ? tile_lim(j + 1) : 0;
     const uint8_t* Kn = kslot_p(jp, j, 1);
     const uint8_t* Vs = vslot_p(jp, j, 0);
-    reset_max();
+    pm[0] = pm[1] = kNegInf;
 
-    // phase X: S of tile j+1 | query block 1 of tile j
-    bf16x8 kf[QK8 ? 1 : nKF];
+    // phase X: S of tile j+1 | key half 1 of tile j
+    bf16x8 kf[QK8 ? 1 : NX];
     i32x8 kf8[QK8 ? nKF8 : 1];
     uint32_t ksc[2] = {0u, 0u};
     if constexpr (!QK8) {
@@ -533,12 +416,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
       // the products read the scales a few instructions after the VALU shift wrote them
       asm volatile("s_nop 4" : "+v"(ksc[0]), "+v"(ksc[1]));
     }
-    bf16x8 vf[nVF];
+    bf16x8 vf[NY];
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, S::NX>([&](auto ic) {
+    static_for<0, NX>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      constexpr int f = i >> 1, qb = i & 1, kb = f / nK, kk = f % nK;
-      if constexpr (!QK8 && qb == 0 && f + 2 < nKF) kf[f + 2] = k_frag(Kn, f + 2);
+      constexpr int kb = i / nK, kk = i % nK;
+      if constexpr (!QK8 && i + 2 < NX) kf[i + 2] = k_frag(Kn, i + 2);
       // loads of K j+2 and V j+1, one per odd step (past the last tile, K j+2 loads zeros
       // into a slot nobody reads any more)
       if constexpr ((i & 1) && (i >> 1) < LK) {
@@ -549,59 +432,62 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
       }
       if constexpr ((i & 1) && (i >> 1) >= LK && (i >> 1) < LK + Tl::loadsPerWave)
         ld.issue(vslot_p(jp, j, 1), Vr, (j + 1) * kBlockN, T, (i >> 1) - LK);
-      if constexpr (i == S::NX - 2) {
+      if constexpr (i == NX - 2) {
         vf[0] = v_frag(Vs, 0);
         vf[1] = v_frag(Vs, 1);
       }
       if constexpr (!QK8) {
-        if constexpr (kk == 0) mfma_s_first(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
-        else mfma_s(sblk(nxt, qb, kb), kf[f], qf[qb][kk]);
+        if constexpr (kk == 0) mfma_s_first(sblk(nxt, kb), kf[i], qf[kk]);
+        else mfma_s(sblk(nxt, kb), kf[i], qf[kk]);
       } else if constexpr (i % 4 == 0) {
-        // one E4M3 product every fourth step: m = i / 4 -> query block m % 2, fragment m / 2
-        constexpr int m = i / 4, qb8 = m & 1, f8 = m >> 1, kb8 = f8 / nK8, kk8 = f8 % nK8;
-        if constexpr (qb8 == 0 && f8 + 2 < nKF8) kf8[f8 + 2] = k_frag8(Kn, f8 + 2);
-        mfma8_s<kk8 == 0, 2 * kk8>(sblk(nxt, qb8, kb8), kf8[f8], qf8[qb8][kk8], ksc[kb8], qsc[qb8]);
+        // one E4M3 product every fourth step: fragment m = i / 4
+        constexpr int m = i / 4, kb8 = m / nK8, kk8 = m % nK8;
+        if constexpr (m + 2 < nKF8) kf8[m + 2] = k_frag8(Kn, m + 2);
+        mfma8_s<kk8 == 0, 2 * kk8>(sblk(nxt, kb8), kf8[m], qf8[kk8], ksc[kb8], qsc);
       }
-      if constexpr (i == S::XM0) fence2(sblk(nxt, 0, 0), sblk(nxt, 1, 0));
-      static_for<32, 64>([&](auto vc) {
+      // the step's VALU work follows its product, so consecutive products are evenly spaced
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == S::XM0) fence1(sblk(nxt, 0));
+      static_for<16, 32>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
         if constexpr (S::x_exp(v) == i) exp_item(cur, v, MASK);
         if constexpr (S::x_sum(v) == i) sum_item(cur, v);
       });
-      static_for<4, 8>([&](auto cc_) {
+      static_for<2, 4>([&](auto cc_) {
         constexpr int ch = decltype(cc_)::value;
-        if constexpr (S::x_pack(ch) == i) pack_item(cur, cur, ch);
+        if constexpr (S::x_pack(ch) == i) pack_item(cur, ch);
       });
       if constexpr (i == S::XF) fold();
-      static_for<0, 16>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if constexpr (S::x_max(u) == i) max_item(nxt, u >> 3, 0, u & 7, MASK, lim);
+      static_for<0, 8>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (S::x_max(t) == i) max_item(nxt, 0, t, MASK, lim);
       });
       __builtin_amdgcn_sched_barrier(0);
     });
 
-    // phase Y: P V of tile j | max, reference update and query block 0 of tile j+1
-    float m_old[2];
+    // phase Y: P V of tile j | max, reference update and key half 0 of tile j+1
+    float m_old = 0.f;
     bool any = false;
-    static_for<0, S::NY>([&](auto ic) {
+    static_for<0, NY>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      constexpr int g = i >> 1, qb = i & 1, cc = g / nD, db = g % nD;
-      if constexpr (qb == 0 && g + 2 < nVF) vf[g + 2] = v_frag(Vs, g + 2);
-      mfma_o(acc[qb][db], vf[g], pop(cur, qb, cc));
-      if constexpr (i == S::YM0) fence2(sblk(nxt, 0, 1), sblk(nxt, 1, 1));
-      static_for<0, 16>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if constexpr (S::y_max(u) == i) max_item(nxt, u >> 3, 1, u & 7, MASK, lim);
+      constexpr int cc = i / nD, db = i % nD;
+      if constexpr (i + 2 < NY) vf[i + 2] = v_frag(Vs, i + 2);
+      mfma_o(acc[db], vf[i], p[cc]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == S::YM0) fence1(sblk(nxt, 1));
+      static_for<0, 8>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (S::y_max(t) == i) max_item(nxt, 1, t, MASK, lim);
       });
       if constexpr (i == S::YR) any = reduce(m_old);
-      static_for<0, 32>([&](auto vc) {
+      static_for<0, 16>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
         if constexpr (S::y_exp(v) == i) exp_item(nxt, v, MASK);
         if constexpr (S::y_sum(v) == i) sum_item(nxt, v);
       });
-      static_for<0, 4>([&](auto cc_) {
+      static_for<0, 2>([&](auto cc_) {
         constexpr int ch = decltype(cc_)::value;
-        if constexpr (S::y_pack(ch) == i) pack_item(nxt, nxt, ch);
+        if constexpr (S::y_pack(ch) == i) pack_item(nxt, ch);
       });
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -615,53 +501,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     __syncthreads();
   };
 
-  // ---- last tile: finish query block 1 and multiply (no next tile) -------------------------
+  // ---- last tile: finish key half 1 and multiply (no next tile) ----------------------------
   auto last = [&](auto cur, int j) {
     const uint8_t* Vs = vslot(j);
 #pragma unroll
-    for (int v = 32; v < 64; ++v) exp_item(cur, v, true);
+    for (int v = 16; v < 32; ++v) exp_item(cur, v, true);
 #pragma unroll
-    for (int v = 32; v < 64; ++v) sum_item(cur, v);
-#pragma unroll
-    for (int ch = 4; ch < 8; ++ch) pack_item(cur, cur, ch);
+    for (int v = 16; v < 32; ++v) sum_item(cur, v);
+    pack_item(cur, 2);
+    pack_item(cur, 3);
     fold();
     // the products below read P right after the VALU wrote it
-    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p1[0]), "+v"(p1[1]), "+v"(p1[2]), "+v"(p1[3]));
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p[2]), "+v"(p[3]));
 #pragma unroll
-    for (int g = 0; g < nVF; ++g) {
-      const bf16x8 a = v_frag(Vs, g);
-      const int cc = g / nD, db = g % nD;
-      mfma_o(acc[0][db], a, pop(cur, 0, cc));
-      mfma_o(acc[1][db], a, pop(cur, 1, cc));
-    }
+    for (int g = 0; g < NY; ++g) mfma_o(acc[g % nD], v_frag(Vs, g), p[g / nD]);
   };
 
-  // ---- prologue: tile 0's scores, max and query block 0 ---------------------------------
+  // ---- prologue: tile 0's scores, max and key half 0 -------------------------------------
   if constexpr (!QK8) {
     ld.issue_all(kslot(0), Kr, 0, T);
-    ld.issue_all(vslot(0), Vr, 0, T);
     if (ntiles > 1) ld.issue_all(kslot(1), Kr, kBlockN, T);
   } else {
     ld8.issue_all(kslot(0), Kr8, Ksr, 0, T);
-    ld.issue_all(vslot(0), Vr, 0, T);
     if (ntiles > 1) ld8.issue_all(kslot(1), Kr8, Ksr, kBlockN, T);
   }
+  ld.issue_all(vslot(0), Vr, 0, T);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   {
     const uint8_t* K0 = kslot(0);
     if constexpr (!QK8) {
 #pragma unroll
-      for (int f = 0; f < nKF; ++f) {
+      for (int f = 0; f < NX; ++f) {
         const bf16x8 a = k_frag(K0, f);
         const int kb = f / nK, kk = f % nK;
-        if (kk == 0) {
-          mfma_s_first(s0[kb], a, qf[0][kk]);
-          mfma_s_first(s1a[kb], a, qf[1][kk]);
-        } else {
-          mfma_s(s0[kb], a, qf[0][kk]);
-          mfma_s(s1a[kb], a, qf[1][kk]);
-        }
+        f32x16& dst = kb ? s1a : s0;
+        if (kk == 0) mfma_s_first(dst, a, qf[kk]);
+        else mfma_s(dst, a, qf[kk]);
       }
     } else {
       uint32_t ksc0[2] = {k_scale(K0, 0), k_scale(K0, 1)};
@@ -669,31 +545,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
       static_for<0, nKF8>([&](auto fc) {
         constexpr int f = decltype(fc)::value, kb = f / nK8, kk = f % nK8;
         const i32x8 a = k_frag8(K0, f);
-        mfma8_s<kk == 0, 2 * kk>(s0[kb], a, qf8[0][kk], ksc0[kb], qsc[0]);
-        mfma8_s<kk == 0, 2 * kk>(s1a[kb], a, qf8[1][kk], ksc0[kb], qsc[1]);
+        mfma8_s<kk == 0, 2 * kk>(kb ? s1a : s0, a, qf8[kk], ksc0[kb], qsc);
       });
     }
-    fence2(s0[0], s1a[0]);
-    fence2(s0[1], s1a[1]);
+    fence1(s0);
+    fence1(s1a);
     const bool masked = nfull == 0;
-    int lim[2];
-    tile_lim(0, lim);
-    reset_max();
+    const int lim = tile_lim(0);
+    pm[0] = pm[1] = kNegInf;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) max_item(Par<0>{}, u >> 4, (u >> 3) & 1, u & 7, masked, lim);
-    float a = fmaxf(pm[0][0], pm[0][1]), b = fmaxf(pm[1][0], pm[1][1]);
-    halves_max2(a, b, h);
+    for (int u = 0; u < 16; ++u) max_item(Par<0>{}, u >> 3, u & 7, masked, lim);
     // a row that sees no key of tile 0 keeps -inf here; its exponentials are all masked to 0
-    m_ref[0] = a;
-    m_ref[1] = b;
-    mc[0] = a * c;
-    mc[1] = b * c;
+    m_ref = halves_max1(fmaxf(pm[0], pm[1]));
+    mc = m_ref * c;
 #pragma unroll
-    for (int v = 0; v < 32; ++v) exp_item(Par<0>{}, v, masked);
+    for (int v = 0; v < 16; ++v) exp_item(Par<0>{}, v, masked);
 #pragma unroll
-    for (int v = 0; v < 32; ++v) sum_item(Par<0>{}, v);
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) pack_item(Par<0>{}, Par<0>{}, ch);
+    for (int v = 0; v < 16; ++v) sum_item(Par<0>{}, v);
+    pack_item(Par<0>{}, 0);
+    pack_item(Par<0>{}, 1);
   }
   // every wave is done with kslot(0) before iteration 0 refills it
   __syncthreads();
@@ -703,57 +573,47 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(const FwdKArgs ar
     iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
     iteration(Par<1>{}, Par<0>{}, j + 1, Flag<false>{}, IC<1>{});
   }
-  // tile j + 1 may still need no mask (the pairs above stop one tile early): one more unmasked
-  // iteration, after which tile j + 1's buffers move to the even set the masked tail expects
+  // one more unmasked iteration when tile j + 1 needs no mask, after which tile j + 1's key
+  // half 1 moves to the even buffer the masked tail expects
   if (j + 1 < nfull) {
     iteration(Par<0>{}, Par<1>{}, j, Flag<false>{}, IC<0>{});
-    s1a[0] = s1b[0];
-    s1a[1] = s1b[1];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) p0a[cc] = p0b[cc];
+    s1a = s1b;
     ++j;
   }
-  // masked tail (at most four tiles): one body, the next tile's block-1 scores and block-0
-  // P are moved into the even buffers after each iteration so the roles never alternate
+  // masked tail (at most the diagonal tiles): one body, the next tile's key half 1 moved into
+  // the even buffer after each iteration so the roles never alternate
   for (; j + 1 < ntiles; ++j) {
     iteration(Par<0>{}, Par<1>{}, j, Flag<true>{}, IC<-1>{});
-    s1a[0] = s1b[0];
-    s1a[1] = s1b[1];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) p0a[cc] = p0b[cc];
+    s1a = s1b;
   }
   last(Par<0>{}, j);
 
   fence_acc(acc);
+  const float l_half = lp[0] + lp[1];
+  const float r_half = rp[0] + rp[1];
+  const float l_tot = l_half + swap_halves(l_half);
+  const float r_tot = r_half + swap_halves(r_half);
+  if (qrow < Tq) {
+    // a row that sees no key at all (causal, fewer keys than queries) gets O = 0, LSE = -inf
+    const float inv = r_tot > 0.f ? 1.0f / r_tot : 0.f;
+    uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = qw0 + 32 * qb + l32;
-    const float l_half = lp[qb][0] + lp[qb][1];
-    const float r_half = rp[qb][0] + rp[qb][1];
-    const float l_tot = l_half + swap_halves(l_half);
-    const float r_tot = r_half + swap_halves(r_half);
-    if (qrow < Tq) {
-      // a row that sees no key at all (causal, fewer keys than queries) gets O = 0, LSE = -inf
-      const float inv = r_tot > 0.f ? 1.0f / r_tot : 0.f;
-      uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
+    for (int db = 0; db < nD; ++db) {
 #pragma unroll
-      for (int db = 0; db < nD; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = db * 32 + 8 * g + 4 * h;
-          u32x2 w = {pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv),
-                     pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * h;
+        u32x2 w = {pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
+                   pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
-      if (h == 0) Lh[qrow] = l_tot > 0.f ? (m_ref[qb] * c + log2_fast(l_tot)) * kLn2 : kNegInf;
     }
+    if (h == 0) Lh[qrow] = l_tot > 0.f ? (m_ref * c + log2_fast(l_tot)) * kLn2 : kNegInf;
   }
 }
 
 template <int D, bool CAUSAL, bool QK8>
 hipError_t launch(const FwdBf16Problem& p) {
-  FwdKArgs k;
+  FwdKArgs k{};
   k.q8 = static_cast<const uint8_t*>(p.q8);
   k.k8 = static_cast<const uint8_t*>(p.k8);
   k.qs = static_cast<const uint8_t*>(p.q_scale);
@@ -790,7 +650,7 @@ hipError_t launch(const FwdBf16Problem& p) {
     k.lse_bs = (int64_t)p.Hq * p.Tq;
   }
   k.c = p.scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, QK8>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
+  hipLaunchKernelGGL((fwd_q32_kernel<D, CAUSAL, QK8>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
   return hipGetLastError();
 }
 
@@ -801,7 +661,8 @@ hipError_t launch_fwd_bf16_general(const FwdBf16Problem& p) {
     if (p.D == 64) return p.causal ? launch<64, true, true>(p) : launch<64, false, true>(p);
     return p.causal ? launch<128, true, true>(p) : launch<128, false, true>(p);
   }
-  return launch_fwd_bf16_q32(p);
+  if (p.D == 64) return p.causal ? launch<64, true, false>(p) : launch<64, false, false>(p);
+  return p.causal ? launch<128, true, false>(p) : launch<128, false, false>(p);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {

@@ -1,8 +1,10 @@
-// Pieces shared by the forward kernels: matrix-core products with explicit register files,
-// wait-state fences, compile-time loops, cross-half row maxima and the kernel arguments.
+// Pieces of the forward kernel: matrix-core products with explicit register files (bf16 and
+// E4M3), the E4M3 tile layout and loader, wait-state fences, compile-time loops, the
+// cross-half row maximum and the kernel arguments.
 #pragma once
 
 #include "fa_common.h"
+#include "fa_swz.h"
 
 namespace fa {
 namespace fwd {
@@ -27,23 +29,6 @@ __device__ __forceinline__ void mfma_o(f32x16& d, const bf16x8& a, const bf16x8&
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
-// 20 wait states (more than the result latency of a 32x32x16 product) between the last
-// product writing x and y and any later instruction that uses them.
-__device__ __forceinline__ void fence2(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
-}
-template <int N>
-__device__ __forceinline__ void fence_acc(f32x16 (&a)[2][N]) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < N; ++db) asm volatile("" : "+a"(a[qb][db]));
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < N; ++db) asm volatile("" : "+a"(a[qb][db]));
-}
 
 template <bool B>
 struct Flag {
@@ -67,28 +52,6 @@ struct Par {
   static constexpr int value = P;
 };
 
-// v_permlane32_swap_b32 x, y: lanes 32-63 of x trade places with lanes 0-31 of y, so x
-// becomes [x_lo | y_lo] and y becomes [x_hi | y_hi]. Inline asm: with this toolchain the
-// builtin returns its first result for both results. Both swaps sit in one block between
-// s_nop padding: read before the VALU writes of its operands had reached every lane, the
-// swap returned stale upper lanes.
-__device__ __forceinline__ void permlane32_swap2(float& x, float& y, float& u, float& w) {
-  asm volatile(
-      "s_nop 7\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\ts_nop 7"
-      : "+v"(x), "+v"(y), "+v"(u), "+v"(w));
-}
-
-// Full-row maxima of two rows held as key halves in lanes l and l ^ 32 (a: query block 0,
-// b: query block 1): swap(a, b) puts row a's halves side by side in lanes 0-31 and row b's
-// in lanes 32-63, swap(b, a) the other way round.
-__device__ __forceinline__ void halves_max2(float& a, float& b, int h) {
-  float x = a, y = b, u = b, w = a;
-  permlane32_swap2(x, y, u, w);
-  const float f = fmaxf(x, y);   // lanes 0-31: row a, lanes 32-63: row b
-  const float g = fmaxf(u, w);   // lanes 0-31: row b, lanes 32-63: row a
-  a = h ? g : f;
-  b = h ? f : g;
-}
 
 // Item x of n items is done at step s0 + x (s1 - s0) / n of its window [s0, s1).
 constexpr int win_step(int x, int n, int s0, int s1) { return s0 + x * (s1 - s0) / n; }
@@ -116,9 +79,89 @@ struct FwdKArgs {
   const uint8_t *q8, *k8, *qs, *ks;
 };
 
-// fence_acc for the accumulators of one query block
+// E4M3 variant of the S products: 32 x 32 x 64 with a power-of-two scale per 32 k-values.
+// Lane l supplies row (A) / column (B) l % 32; its bytes 0-15 are k-values 16 (l / 32) + 0..15
+// of the first 32-value block and bytes 16-31 the same positions of the second block; the
+// scale of block q of a row comes from lane row + 32 q, byte BYTE of its scale register
+// (op_sel carries bit 0 of BYTE, op_sel_hi bit 1).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <bool FIRST, int BYTE>
+__device__ __forceinline__ void mfma8_s(f32x16& d, const i32x8& a, const i32x8& b, uint32_t sa,
+                                        uint32_t sb) {
+  static_assert(BYTE == 0 || BYTE == 2, "scale byte");
+  if constexpr (FIRST && BYTE == 0)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4"
+                 : "=&v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+  else if constexpr (FIRST)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[1,1,0]"
+                 : "=&v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+  else if constexpr (BYTE == 0)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4"
+                 : "+v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+  else
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[1,1,0]"
+                 : "+v"(d) : "v"(a), "a"(b), "v"(sa), "v"(sb));
+}
+
+// A [64 x D] E4M3 tile in LDS (D bytes a row, 16-byte chunks XOR-swizzled so that 8 (D = 128)
+// or 4 (D = 64) consecutive rows reading one logical chunk hit distinct banks for 32 and for
+// 64 banks), followed by its block-scale bytes: D / 32 per row, in one dword per row (a direct
+// load to LDS of 1 or 2 bytes a lane writes a zero-extended dword a lane).
+template <int D>
+struct SwzTile8 {
+  static constexpr int CH = D / 16;
+  static constexpr int RB = D;
+  static constexpr int SB = D / 32;     // scale bytes per row in HBM
+  static constexpr int sc_offset = 64 * RB;
+  static constexpr int loadsPerWave = 64 * CH / 256;
+  __device__ static __forceinline__ int swz(int row) { return D == 128 ? (row & 7) : ((row >> 1) & 3); }
+  __device__ static __forceinline__ int offset(int row, int lchunk) {
+    return row * RB + ((lchunk ^ swz(row)) << 4);
+  }
+};
+
+// Direct buffer -> LDS loads of a 64-row E4M3 tile and its scales by the 4 waves of a
+// workgroup (the same lane-to-chunk rule as TileLoader; rows at or past T arrive as zeros);
+// wave 0 also moves the 64 rows' scale bytes.
+template <int D>
+struct TileLoader8 {
+  using Tl = SwzTile8<D>;
+  uint32_t vofs[Tl::loadsPerWave];   // byte offset of the lane's i-th chunk from the tile's row 0
+  int wave, lane;
+  uint32_t rsb, srs;   // bytes between rows of the codes and of the scales
+  __device__ __forceinline__ TileLoader8(int wave_, int lane_, int row_stride)
+      : wave(wave_), lane(lane_), rsb((uint32_t)row_stride), srs((uint32_t)row_stride / 32u) {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) {
+      const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
+      const int row = u / Tl::CH;
+      vofs[i] = (uint32_t)row * rsb + (uint32_t)(((u % Tl::CH) ^ Tl::swz(row)) * 16);
+    }
+  }
+  // codes and scales come through buffer resources over the T rows (rows at or past T: zeros)
+  __device__ __forceinline__ void issue(uint8_t* dst, const i32x4& rsrc, int row0, int T,
+                                        int i) const {
+    buf_lds_dma<16>(dst + (wave * Tl::loadsPerWave + i) * 1024, rsrc, vofs[i],
+                    (uint32_t)min(row0, T) * rsb);
+  }
+  __device__ __forceinline__ void issue_scales(uint8_t* dst, const i32x4& srsrc, int row0,
+                                               int T) const {
+    if (wave == 0)
+      buf_lds_dma<Tl::SB>(dst + Tl::sc_offset, srsrc, (uint32_t)lane * srs,
+                          (uint32_t)min(row0, T) * srs);
+  }
+  __device__ __forceinline__ void issue_all(uint8_t* dst, const i32x4& rsrc, const i32x4& srsrc,
+                                            int row0, int T) const {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, rsrc, row0, T, i);
+    issue_scales(dst, srsrc, row0, T);
+  }
+};
+
+// 20 wait states (more than the result latency of a 32x32x16 product) between the last
+// product writing the accumulators and any later instruction that uses them.
 template <int N>
-__device__ __forceinline__ void fence_acc1(f32x16 (&a)[N]) {
+__device__ __forceinline__ void fence_acc(f32x16 (&a)[N]) {
 #pragma unroll
   for (int db = 0; db < N; ++db) asm volatile("" : "+a"(a[db]));
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
@@ -126,8 +169,11 @@ __device__ __forceinline__ void fence_acc1(f32x16 (&a)[N]) {
   for (int db = 0; db < N; ++db) asm volatile("" : "+a"(a[db]));
 }
 
-// Full-row maximum of one row held as key halves in lanes l and l ^ 32: after the swap of
-// two copies, x holds lanes 0-31 of the row's value in both halves and y lanes 32-63.
+// Full-row maximum of one row held as key halves in lanes l and l ^ 32. v_permlane32_swap_b32
+// x, y trades lanes 32-63 of x with lanes 0-31 of y; on two copies of the value, x then holds
+// lanes 0-31 in both halves and y lanes 32-63. Inline asm: with this toolchain the builtin
+// returns its first result for both results. The swap sits between s_nop padding: read before
+// the VALU writes of its operands had reached every lane, it returned stale upper lanes.
 __device__ __forceinline__ float halves_max1(float a) {
   float x = a, y = a;
   asm volatile("s_nop 7\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 7" : "+v"(x), "+v"(y));

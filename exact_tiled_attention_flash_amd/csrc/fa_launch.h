@@ -68,8 +68,6 @@ struct DecodeBf16Problem {
 
 hipError_t launch_fwd_bf16(const FwdArgs &a);
 hipError_t launch_fwd_bf16_general(const FwdBf16Problem &p);
-// bf16 Q K^T only (p.q8 null): one 32-query block per wave, two workgroups per compute unit
-hipError_t launch_fwd_bf16_q32(const FwdBf16Problem &p);
 hipError_t launch_fwd_f32(const FwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a);
 hipError_t launch_decode_bf16(const DecodeBf16Problem &p);
