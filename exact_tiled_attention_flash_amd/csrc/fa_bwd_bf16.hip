@@ -171,67 +171,100 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const float* dvec = reinterpret_cast<const float*>(st + St::dvec);
     const int q0 = qt * kQTile;
 
+    // Both 32-query blocks in one pipelined body: block 0's scores are worked through under
+    // block 1's S and dP products, and block 1's under block 0's dV and dK products. A block
+    // wholly before this wave's keys (causal) runs masked and contributes zeros.
+    bool nm[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qb0 = q0 + qb * 32;
-      if (CAUSAL && qb0 + 31 < kw0) continue;  // every query of the block precedes every key
-      f32x16 s = f32x16{}, dp = f32x16{};
-      // operand fragments are read two k-steps ahead of their products (left to itself the
-      // compiler reads each one just before its product and waits out the LDS latency)
-      bf16x8 qa[nK], da[nK];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        qa[kk] = row_operand<D>(Qs, qb * 32 + l32, 2 * kk + h);
-        da[kk] = row_operand<D>(dOs, qb * 32 + l32, 2 * kk + h);
-      }
-#pragma unroll
-      for (int kk = 0; kk < nK; ++kk) {
-        if (kk + 2 < nK) {
-          qa[kk + 2] = row_operand<D>(Qs, qb * 32 + l32, 2 * (kk + 2) + h);
-          da[kk + 2] = row_operand<D>(dOs, qb * 32 + l32, 2 * (kk + 2) + h);
-        }
-        s = mfma32(qa[kk], kf[kk], s);
-        dp = mfma32(da[kk], vf[kk], dp);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the first transposed operands of dV and dK load under the softmax work below
-      constexpr int nT = 2 * nD;   // products per tensor: (db, cc), cc fastest
-      bf16x8 ta[nT], tb[nT];
-      ta[0] = tr_operand<D>(dOs, 0, qb * 32, lane);
-      tb[0] = tr_operand<D>(Qs, 0, qb * 32, lane);
-      // lane = key; register r = query qb0 + 8*(r/4) + 4h + (r%4)
-      const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > T);
-      f32x16 p, ds;
+      nm[qb] = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > T);
+    }
+    // s / dp hold S and dP, then P and dS in place
+    f32x16 s[2], dp[2];
+    f32x4 l4[2][4], d4[2][4];
+    bf16x8 pb[2][2], dsb[2][2];
+    auto stats = [&](int qb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qb * 32 + 8 * g + 4 * h);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dvec + qb * 32 + 8 * g + 4 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          float pv = exp2_fast(fmaf(s[r], c, -l4[i]));
-          if (need_mask) {
-            const int qi = qb0 + 8 * g + 4 * h + i;
-            const bool ok = qi < T && (!CAUSAL || key <= qi);
-            pv = ok ? pv : 0.f;
-          }
-          p[r] = pv;
-          ds[r] = pv * (dp[r] - d4[i]);
-        }
+        l4[qb][g] = *reinterpret_cast<const f32x4*>(lse2 + qb * 32 + 8 * g + 4 * h);
+        d4[qb][g] = *reinterpret_cast<const f32x4*>(dvec + qb * 32 + 8 * g + 4 * h);
       }
-      const bf16x8 pb[2] = {pack8(p, 0), pack8(p, 8)};
-      const bf16x8 dsb[2] = {pack8(ds, 0), pack8(ds, 8)};
-#pragma unroll
-      for (int t = 0; t < nT; ++t) {
-        const int db = t / 2, cc = t % 2;
-        if (t + 1 < nT) {
-          ta[t + 1] = tr_operand<D>(dOs, (t + 1) / 2, qb * 32 + 16 * ((t + 1) % 2), lane);
-          tb[t + 1] = tr_operand<D>(Qs, (t + 1) / 2, qb * 32 + 16 * ((t + 1) % 2), lane);
-        }
-        dv[db] = mfma32(ta[t], pb[cc], dv[db]);
-        dk[db] = mfma32(tb[t], dsb[cc], dk[db]);
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // one score of block qb: P = exp2(S c - LSE log2 e), dS = P (dP - D); lane = key, register
+    // r = query q0 + 32 qb + 8 (r / 4) + 4 h + (r % 4)
+    auto item = [&](int qb, int r) {
+      const int g = r >> 2, i = r & 3;
+      float pv = exp2_fast(fmaf(s[qb][r], c, -l4[qb][g][i]));
+      if (nm[qb]) {
+        const int qi = q0 + 32 * qb + 8 * g + 4 * h + i;
+        const bool ok = qi < T && (!CAUSAL || key <= qi);
+        pv = ok ? pv : 0.f;
       }
+      s[qb][r] = pv;
+      dp[qb][r] = pv * (dp[qb][r] - d4[qb][g][i]);
+    };
+    auto pack = [&](int qb, int cc) {
+      pb[qb][cc] = pack8(s[qb], 8 * cc);
+      dsb[qb][cc] = pack8(dp[qb], 8 * cc);
+    };
+    stats(0);
+    // S and dP of both blocks, product f = nK qb + kk; operands read two products ahead (left
+    // to itself the compiler reads each one just before its product and waits out the LDS
+    // latency)
+    constexpr int nF = 2 * nK;
+    bf16x8 qa[nF], da[nF];
+    auto rd = [&](int f) {
+      qa[f] = row_operand<D>(Qs, (f / nK) * 32 + l32, 2 * (f % nK) + h);
+      da[f] = row_operand<D>(dOs, (f / nK) * 32 + l32, 2 * (f % nK) + h);
+    };
+    rd(0);
+    rd(1);
+#pragma unroll
+    for (int f = 0; f < nF; ++f) {
+      const int qb = f / nK, kk = f % nK;
+      if (f + 2 < nF) rd(f + 2);
+      if (kk == 0) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+      }
+      s[qb] = mfma32(qa[f], kf[kk], s[qb]);
+      dp[qb] = mfma32(da[f], vf[kk], dp[qb]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (f == nK / 2) stats(1);
+      if (qb == 1) {
+#pragma unroll
+        for (int r = (kk * 16) / nK; r < ((kk + 1) * 16) / nK; ++r) item(0, r);
+        if (kk == nK / 2 - 1) pack(0, 0);
+        if (kk == nK - 1) pack(0, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dV and dK of both blocks, product t = nT qb + 2 db + cc, transposed operands read two
+    // products ahead
+    constexpr int nT = 2 * nD;
+    bf16x8 ta[2 * nT], tb[2 * nT];
+    auto rdt = [&](int t) {
+      const int qb = t / nT, tt = t % nT;
+      ta[t] = tr_operand<D>(dOs, tt / 2, qb * 32 + 16 * (tt % 2), lane);
+      tb[t] = tr_operand<D>(Qs, tt / 2, qb * 32 + 16 * (tt % 2), lane);
+    };
+    rdt(0);
+    rdt(1);
+#pragma unroll
+    for (int t = 0; t < 2 * nT; ++t) {
+      const int qb = t / nT, tt = t % nT, db = tt / 2, cc = tt % 2;
+      if (t + 2 < 2 * nT) rdt(t + 2);
+      dv[db] = mfma32(ta[t], pb[qb][cc], dv[db]);
+      dk[db] = mfma32(tb[t], dsb[qb][cc], dk[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (qb == 0) {
+#pragma unroll
+        for (int r = (tt * 16) / nT; r < ((tt + 1) * 16) / nT; ++r) item(1, r);
+        if (tt == nT / 2 - 1) pack(1, 0);
+        if (tt == nT - 1) pack(1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

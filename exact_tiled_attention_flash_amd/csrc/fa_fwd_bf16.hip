@@ -76,9 +76,9 @@ struct Sched1 {
   static constexpr int nK = D / 16, nD = D / 32;
   static constexpr int NX = 2 * nK;   // phase X steps (S products, f = nK kb + kk)
   static constexpr int NY = 4 * nD;   // phase Y steps (P V products, g = nD cc + db)
-  static constexpr int XE0 = 0, XE1 = NX - 4, XS0 = 1, XS1 = NX - 2;
+  static constexpr int XE0 = 0, XE1 = NX - 3, XS0 = 1, XS1 = NX - 1;
   static constexpr int XM0 = nK + 2, XM1 = NX;
-  static constexpr int YM0 = 2, YM1 = 2 + NY / 8, YR = YM1, YE0 = YR + 1, YE1 = NY - 2;
+  static constexpr int YM0 = 2, YM1 = 3, YR = YM1, YE0 = YR + 1, YE1 = NY - 1;
   static constexpr int YS0 = YE0 + 1, YS1 = NY;
   static constexpr int x_exp(int v) { return win_step(v - 16, 16, XE0, XE1); }   // v in [16, 32)
   static constexpr int x_sum(int v) { return win_step(v - 16, 16, XS0, XS1); }
