@@ -121,7 +121,7 @@ struct SwzTile8 {
 };
 
 // Direct buffer -> LDS loads of a 64-row E4M3 tile and its scales by the 4 waves of a
-// workgroup (the same lane-to-chunk rule as TileLoader; rows at or past T arrive as zeros);
+// workgroup (the same lane-to-chunk rule as BufTileLoader; rows at or past T arrive as zeros);
 // wave 0 also moves the 64 rows' scale bytes.
 template <int D>
 struct TileLoader8 {

@@ -1,4 +1,4 @@
-// 64-row bf16 tiles in LDS, loaded directly from HBM (global_load_lds_dwordx4) and read as
+// 64-row bf16 tiles in LDS, loaded directly from HBM (buffer -> LDS loads) and read as
 // matrix-core operands, row-major or transposed (ds_read_b64_tr_b16).
 #pragma once
 
@@ -73,50 +73,15 @@ struct SwzTile {
   }
 };
 
-// Direct HBM -> LDS loads of 64-row tiles of a (rows x D) matrix by the 4 waves of a
-// workgroup. Lane `lane` of load i of wave `wave` fills tile bytes [16 u, 16 u + 16),
-// u = (wave * loadsPerWave + i) * 64 + lane, i.e. physical chunk u % CH of row u / CH, with
-// the logical chunk the swizzle maps there. The lane's rows and in-row byte offsets do not
-// depend on the tile and are computed once; per load only the row clamp and one multiply-add
-// remain. Rows at or beyond T are clamped to row T - 1; callers mask or never store
-// whatever depends on them. `wave` must be wave-uniform (it selects the LDS destination); rows
-// of the source are `row_stride` elements apart (D for a (rows x D) matrix, H*D for one head
-// of a packed (rows, H, D) array), and rows up to T of one source stay below 2^31 bytes.
-template <int D>
-struct TileLoader {
-  using Tl = SwzTile<D>;
-  int row[Tl::loadsPerWave];        // tile row of the lane's i-th chunk
-  uint32_t cofs[Tl::loadsPerWave];  // byte offset of that chunk within its row
-  int wave;
-  uint32_t rsb;                     // bytes between consecutive rows of the source matrix
-  __device__ __forceinline__ TileLoader(int wave_, int lane, int row_stride = D)
-      : wave(wave_), rsb((uint32_t)row_stride * 2u) {
-#pragma unroll
-    for (int i = 0; i < Tl::loadsPerWave; ++i) {
-      const int u = (wave * Tl::loadsPerWave + i) * 64 + lane;
-      row[i] = u / Tl::CH;
-      cofs[i] = (uint32_t)(((u % Tl::CH) ^ Tl::swz(row[i])) * 16);
-    }
-  }
-  // load i of rows [row0, row0 + 64) of src into the tile at dst
-  __device__ __forceinline__ void issue(uint8_t* dst, const uint16_t* __restrict__ src, int row0,
-                                        int T, int i) const {
-    // 32-bit byte offset from the wave-uniform base (one head is below 2^31 bytes)
-    const uint32_t off = (uint32_t)min(row0 + row[i], T - 1) * rsb + cofs[i];
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(src) + off,
-                                     (lds_void*)(dst + (wave * Tl::loadsPerWave + i) * 1024), 16,
-                                     0, 0);
-  }
-  __device__ __forceinline__ void issue_all(uint8_t* dst, const uint16_t* __restrict__ src, int row0,
-                                            int T) const {
-#pragma unroll
-    for (int i = 0; i < Tl::loadsPerWave; ++i) issue(dst, src, row0, T, i);
-  }
-};
-
-// The loads of TileLoader through a buffer resource over the source's T rows (rows_rsrc):
-// each lane's offset within the tile is fixed, the tile's first row goes into the scalar
-// offset, and rows at or past T arrive as zeros. No per-load vector arithmetic remains.
+// Direct buffer -> LDS loads of 64-row tiles of a (rows x D) matrix by the 4 waves of a
+// workgroup, through a buffer resource over the source's T rows (rows_rsrc). Lane `lane` of
+// load i of wave `wave` fills tile bytes [16 u, 16 u + 16), u = (wave * loadsPerWave + i) * 64
+// + lane, i.e. physical chunk u % CH of row u / CH, with the logical chunk the swizzle maps
+// there. Each lane's offset within the tile is fixed, the tile's first row goes into the
+// scalar offset, and rows at or past T arrive as zeros: no per-load vector arithmetic remains.
+// `wave` must be wave-uniform (it selects the LDS destination); rows of the source are
+// `row_stride` elements apart (D for a (rows x D) matrix, H*D for one head of a packed
+// (rows, H, D) array), and rows up to T of one source stay below 2^31 bytes.
 template <int D>
 struct BufTileLoader {
   using Tl = SwzTile<D>;
