@@ -15,8 +15,10 @@ cache (batch 1, 32 query heads over 8 K/V heads; also a batch of 8 with valid
 lengths of 1k to 32k keys) in GB/s against the HBM peak, beside the forward
 kernel's time on the same cache; and the forward with block-scaled E4M3 Q and K for Q K^T on
 the headline workload (TFLOP/s, with and without the quantization of Q and K, and its
-difference from the bf16 kernel's O and LSE). The CPU baseline times the float64 oracle on a bounded sample of
-the forward workload (whole (b, h) heads) on the host cores.
+difference from the bf16 kernel's O and LSE). "library_gemm" times the vendor library's bf16 GEMM
+(8192^3) in the same process, as the dense bf16 rate reachable on this GPU at its sustained
+clock. The CPU baseline times the float64 oracle on a bounded sample of the forward workload
+(whole (b, h) heads) on the host cores.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -60,6 +62,20 @@ def _time_launches(torch, fn, steps, warmup):
     per = [a.elapsed_time(b) for a, b in ev]
     total = ev[0][0].elapsed_time(ev[-1][1])
     return total, per, wall_ms
+
+
+def library_gemm(torch, peak):
+    """Context for the roofline: the vendor library's dense bf16 GEMM (8192^3 through
+    torch.matmul, i.e. hipBLASLt) on the same GPU in the same process. Under sustained matrix
+    work the chip clocks below the 2.4 GHz the published peak assumes; this is the dense bf16
+    rate a library reaches here."""
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    ms = _time_loop(torch, lambda: torch.matmul(a, b), 20, 5)
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"op": "bf16 GEMM 8192x8192x8192 (torch.matmul -> hipBLASLt)", "ms": round(ms, 4),
+            "tflops": round(tflops, 1), "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)}
 
 
 def _time_loop(torch, fn, steps, warmup):
@@ -251,6 +267,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true")
+    ap.add_argument("--no-library-gemm", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (counter calibration under rocprofv3)")
@@ -346,6 +363,9 @@ def main():
 
     if not args.no_next_rows:
         out["next_rows"] = next_rows(torch, fa, metrics, max(5, args.steps // 2), args.warmup)
+
+    if not args.no_library_gemm:
+        out["library_gemm"] = library_gemm(torch, peak)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d, args.cpu_budget)
