@@ -186,6 +186,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     Ksr = rows_rsrc(args.ks + ko / 32, kv_bytes / 64u);
   }
 
+  // keys seen by the workgroup's last query, and by all of its queries
+  const int kend = CAUSAL ? min(Tk, q0 + qrows + shift) : Tk;
+  const int ntiles = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
+  const int kall = CAUSAL ? min(Tk, q0 + shift + 1) : Tk;
+  const int nfull = kall > 0 ? min(kall / kBlockN, ntiles) : 0;
+
+  if (ntiles == 0) {   // no query of this workgroup sees a key
+    if (qrow < Tq) {
+      uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
+#pragma unroll
+      for (int d0 = 0; d0 < D; d0 += 8)
+        if ((d0 / 8) % 2 == h) *reinterpret_cast<u32x4*>(orow + d0) = u32x4{0u, 0u, 0u, 0u};
+      if (h == 0) Lh[qrow] = kNegInf;
+    }
+    return;
+  }
+
+  // the first tiles' loads go out before the Q loads, so that the two latencies overlap
+  if constexpr (!QK8) {
+    ld.issue_all(kslot(0), Kr, 0, T);
+    if (ntiles > 1) ld.issue_all(kslot(1), Kr, kBlockN, T);
+  } else {
+    ld8.issue_all(kslot(0), Kr8, Ksr, 0, T);
+    if (ntiles > 1) ld8.issue_all(kslot(1), Kr8, Ksr, kBlockN, T);
+  }
+  ld.issue_all(vslot(0), Vr, 0, T);
+
   // Q^T fragments, moved into AGPRs: lane holds query qrow, d = 16 kk + 8 h + 0..7. E4M3: codes
   // of k-step kk at d = 64 kk + 16 h + 0..15 and 64 kk + 32 + 16 h + 0..15, and the row's scale
   // bytes shifted so that byte 2 kk is block 2 kk + h (the block whose scale this lane half
@@ -233,22 +260,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     asm volatile("" : "+v"(qsc));
   }
 
-  // keys seen by the workgroup's last query, and by all of its queries
-  const int kend = CAUSAL ? min(Tk, q0 + qrows + shift) : Tk;
-  const int ntiles = kend > 0 ? (kend + kBlockN - 1) / kBlockN : 0;
-  const int kall = CAUSAL ? min(Tk, q0 + shift + 1) : Tk;
-  const int nfull = kall > 0 ? min(kall / kBlockN, ntiles) : 0;
-
-  if (ntiles == 0) {   // no query of this workgroup sees a key
-    if (qrow < Tq) {
-      uint16_t* orow = Oh + (int64_t)qrow * args.q_rs;
-#pragma unroll
-      for (int d0 = 0; d0 < D; d0 += 8)
-        if ((d0 / 8) % 2 == h) *reinterpret_cast<u32x4*>(orow + d0) = u32x4{0u, 0u, 0u, 0u};
-      if (h == 0) Lh[qrow] = kNegInf;
-    }
-    return;
-  }
 
   f32x16 acc[nD];
 #pragma unroll
@@ -518,14 +529,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   };
 
   // ---- prologue: tile 0's scores, max and key half 0 -------------------------------------
-  if constexpr (!QK8) {
-    ld.issue_all(kslot(0), Kr, 0, T);
-    if (ntiles > 1) ld.issue_all(kslot(1), Kr, kBlockN, T);
-  } else {
-    ld8.issue_all(kslot(0), Kr8, Ksr, 0, T);
-    if (ntiles > 1) ld8.issue_all(kslot(1), Kr8, Ksr, kBlockN, T);
-  }
-  ld.issue_all(vslot(0), Vr, 0, T);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   {
