@@ -13,7 +13,8 @@
 //                    tiles from the diagonal down. Per wave: S = Q K^T and dP = dO V^T with
 //                    K, V held in registers (lane = key), then dV^T += dO^T P and
 //                    dK^T += Q^T dS, whose A operands are transposing LDS reads of the
-//                    row-major Q and dO tiles.
+//                    row-major Q and dO tiles. The tile's two 32-query blocks run as one
+//                    pipelined body: one block's exponentials under the other's products.
 //   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key tiles up to
 //                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
