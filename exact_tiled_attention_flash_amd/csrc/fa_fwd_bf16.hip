@@ -22,7 +22,8 @@
 //     share a K/V head, so every K/V tile loaded serves all of them). Causal grid order is
 //     heaviest query tile first; consecutive workgroup ids walk (b, head group) fastest,
 //     which keeps a head's tiles on one XCD (workgroups are dealt to the 8 XCDs round-robin)
-//     so its K and V are shared through that XCD's L2.
+//     so its K and V are shared through that XCD's L2; each XCD takes its heads four at a
+//     time, so that the query tiles reading one head's K and V run together.
 //   * K and V tiles (64 keys) reach LDS by direct buffer -> LDS loads into XOR-swizzled
 //     row-major tiles, two slots each (64 KB a workgroup); K runs one tile ahead of V. The
 //     buffer resource ends at the last key row, so rows past it arrive as zeros and a load
@@ -127,11 +128,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   const int h = lane >> 5;
 
   const float c = args.c;
-  // Workgroup -> (query tile, batch, head group): heaviest causal tiles first, (batch, head
-  // group) fastest. hpw query heads sharing one K/V head, 128 / hpw consecutive queries each.
+  // Workgroup -> (query tile, batch, head group) = (qt, r), hpw query heads sharing one K/V
+  // head, 128 / hpw consecutive queries each. Workgroup L goes to XCD x = L % 8, which takes
+  // every r = x (mod 8). An XCD works through its r in groups of grp: within a group,
+  // heaviest causal tile first and r fastest, so the group's tiles walk the same keys at about
+  // the same time and share each K/V line in the XCD's L2. With grp = 0 the group is all of
+  // the XCD's r.
   const int L = workgroup_id();
-  const int r = L % args.nbhg;
-  int qt = L / args.nbhg;
+  int r, qt;
+  if (args.grp > 0) {
+    const int m = L >> 3, per = args.nq * args.grp;
+    const int gi = m / per, w = m - gi * per;
+    qt = w / args.grp;
+    r = (L & 7) + 8 * (gi * args.grp + w % args.grp);
+  } else {
+    r = L % args.nbhg;
+    qt = L / args.nbhg;
+  }
   if (CAUSAL) qt = args.nq - 1 - qt;
   const int b = r / args.HG, hg = r % args.HG;
   const int hpw = 1 << args.hpw_log2;
@@ -633,6 +646,9 @@ hipError_t launch(const FwdBf16Problem& p) {
   k.HG = p.Hq >> k.hpw_log2;
   k.nbhg = p.B * k.HG;
   k.nq = (p.max_q + (kBlockM >> k.hpw_log2) - 1) / (kBlockM >> k.hpw_log2);
+  // four (batch, head group)s at a time on each XCD: their K and V (2 MB each at T = 4096,
+  // D = 128) stay about within the XCD's 4 MB L2 while all their query tiles read them
+  k.grp = k.nbhg % 32 == 0 ? 4 : 0;
   k.Tq = p.Tq;
   k.Tk = p.Tk;
   if (p.cu_q) {   // packed (rows, heads, D)

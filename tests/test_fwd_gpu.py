@@ -67,6 +67,20 @@ def test_fwd_batch_heads(fa, B, H):
             _compare(o, lse, o_ref, lse_ref, dtype)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fwd_heads_in_groups_of_four_per_xcd(fa, D):
+    """B * H a multiple of 32 takes the grid order that hands each XCD four heads at a time;
+    every head and query tile must still be computed once, in the right place."""
+    B, H, T = 2, 16, 300
+    for causal in (False, True):
+        print(f"case fwd grouped grid B={B} H={H} T={T} D={D} causal={causal}", flush=True)
+        d = synth.make_inputs(B, H, T, D, "bf16", seed=400 + D)
+        o, lse = _run(fa, d, "bf16", causal, 1.0 / math.sqrt(D))
+        o_ref, lse_ref = oracle.attention_forward(*(as_f64(d[n], "bf16") for n in "qkv"),
+                                                  1.0 / math.sqrt(D), causal)
+        _compare(o, lse, o_ref, lse_ref, "bf16", f"causal={causal}")
+
+
 def test_workload_small_f32(fa):
     w = synth.WORKLOADS["fwd_f32_b1h2t128d64"]
     d = synth.make_workload_inputs(w)
