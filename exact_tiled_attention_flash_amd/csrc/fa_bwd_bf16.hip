@@ -105,7 +105,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, float c, float scale) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, int grp, float c,
+    float scale) {
   using St = DkdvStage<D>;
   constexpr int nD = D / 32;
   constexpr int nK = D / 16;
@@ -118,8 +119,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int h = lane >> 5;
 
   const int L = workgroup_id();
-  const int bh = L % BH;
-  const int k0 = (L / BH) * kKeysPerWG;   // key tile 0 (the heaviest when causal) first
+  int bh, kt;
+  xcd_grid_item(L, BH, (T + kKeysPerWG - 1) / kKeysPerWG, grp, bh, kt);
+  const int k0 = kt * kKeysPerWG;   // key tile 0 (the heaviest when causal) first
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
   const size_t base = (size_t)bh * T * D;
@@ -285,7 +287,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
-    uint16_t* __restrict__ dQ, int T, int BH, int nq, float c, float scale) {
+    uint16_t* __restrict__ dQ, int T, int BH, int nq, int grp, float c, float scale) {
   using Tl = SwzTile<D>;
   constexpr int nD = D / 32;
   constexpr int nK = D / 16;
@@ -299,8 +301,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int h = lane >> 5;
 
   const int L = workgroup_id();
-  const int bh = L % BH;
-  int qt = L / BH;
+  int bh, qt;
+  xcd_grid_item(L, BH, nq, grp, bh, qt);
   if (CAUSAL) qt = nq - 1 - qt;  // longest key range first
   const int q0 = qt * kQueriesPerWG;
   const int qw0 = q0 + wave * 32;
@@ -423,11 +425,12 @@ hipError_t launch(const BwdArgs& a) {
   const int nk = (a.T + kKeysPerWG - 1) / kKeysPerWG;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nk * BH), dim3(kThreads), 0, a.stream, q, k,
                      v, dout, dvec, lse2, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv),
-                     a.T, BH, c, a.scale);
+                     a.T, BH, xcd_group(BH), c, a.scale);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int nq = (a.T + kQueriesPerWG - 1) / kQueriesPerWG;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream, q, k,
-                     v, dout, dvec, lse2, static_cast<uint16_t*>(a.dq), a.T, BH, nq, c, a.scale);
+                     v, dout, dvec, lse2, static_cast<uint16_t*>(a.dq), a.T, BH, nq, xcd_group(BH), c,
+                     a.scale);
   return hipGetLastError();
 }
 

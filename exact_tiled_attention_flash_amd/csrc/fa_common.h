@@ -31,6 +31,27 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(lane_thread_id() >> 6);
 }
 
+// Grid order over units (a batch and head, or head group) and their tiles. The 8 XCDs are
+// dealt workgroups round-robin (workgroup L to XCD L % 8), so unit r = x (mod 8) stays on XCD
+// x and its K, V, Q, dO lines are shared through that XCD's L2. With grp > 0 an XCD works
+// through its units grp at a time, tile index slowest within the group, so that the tiles
+// of a unit run together and find its lines still in L2 (4 MB per XCD); grp = 0 takes all
+// of the XCD's units at once (r = L % n_units, tile = L / n_units). grp > 0 needs n_units to
+// be a multiple of 8 grp. Tile 0 comes first; callers reverse it where the heaviest is last.
+__host__ __device__ constexpr int xcd_group(int n_units) { return n_units % 32 == 0 ? 4 : 0; }
+__device__ __forceinline__ void xcd_grid_item(int L, int n_units, int n_tiles, int grp, int& r,
+                                              int& tile) {
+  if (grp > 0) {
+    const int m = L >> 3, per = n_tiles * grp;
+    const int gi = m / per, w = m - gi * per;
+    tile = w / grp;
+    r = (L & 7) + 8 * (gi * grp + w % grp);
+  } else {
+    r = L % n_units;
+    tile = L / n_units;
+  }
+}
+
 // 32x32x16 bf16 matrix-core product, fp32 accumulate: acc += A(32x16) * B(16x32).
 // Operand lane layout: lane l supplies row/column (l % 32) and the 8 k-values of
 // k-half (l / 32). Result: lane l holds column (l % 32), rows

@@ -129,22 +129,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
 
   const float c = args.c;
   // Workgroup -> (query tile, batch, head group) = (qt, r), hpw query heads sharing one K/V
-  // head, 128 / hpw consecutive queries each. Workgroup L goes to XCD x = L % 8, which takes
-  // every r = x (mod 8). An XCD works through its r in groups of grp: within a group,
-  // heaviest causal tile first and r fastest, so the group's tiles walk the same keys at about
-  // the same time and share each K/V line in the XCD's L2. With grp = 0 the group is all of
-  // the XCD's r.
+  // head, 128 / hpw consecutive queries each; heaviest causal tile first. Within an XCD's
+  // group of r the tiles walk the same keys at about the same time and share each K/V line.
   const int L = workgroup_id();
   int r, qt;
-  if (args.grp > 0) {
-    const int m = L >> 3, per = args.nq * args.grp;
-    const int gi = m / per, w = m - gi * per;
-    qt = w / args.grp;
-    r = (L & 7) + 8 * (gi * args.grp + w % args.grp);
-  } else {
-    r = L % args.nbhg;
-    qt = L / args.nbhg;
-  }
+  xcd_grid_item(L, args.nbhg, args.nq, args.grp, r, qt);
   if (CAUSAL) qt = args.nq - 1 - qt;
   const int b = r / args.HG, hg = r % args.HG;
   const int hpw = 1 << args.hpw_log2;
@@ -648,7 +637,7 @@ hipError_t launch(const FwdBf16Problem& p) {
   k.nq = (p.max_q + (kBlockM >> k.hpw_log2) - 1) / (kBlockM >> k.hpw_log2);
   // four (batch, head group)s at a time on each XCD: their K and V (2 MB each at T = 4096,
   // D = 128) stay about within the XCD's 4 MB L2 while all their query tiles read them
-  k.grp = k.nbhg % 32 == 0 ? 4 : 0;
+  k.grp = xcd_group(k.nbhg);
   k.Tq = p.Tq;
   k.Tk = p.Tk;
   if (p.cu_q) {   // packed (rows, heads, D)

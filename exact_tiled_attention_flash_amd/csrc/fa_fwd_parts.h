@@ -73,7 +73,7 @@ struct FwdKArgs {
   int hpw_log2;      // log2 of the query heads per workgroup (1, 2 or 4 heads)
   int nbhg;          // B * HG
   int nq;            // query tiles per (batch, head group)
-  int grp;           // (batch, head group)s an XCD works through together; 0: all of them
+  int grp;           // (batch, head group)s an XCD works through together (xcd_grid_item)
   float c;           // scale * log2(e)
   // E4M3 Q K^T: codes of q / k (same layout and strides as q / k, one byte an element) and
   // their block scales (one byte per 32 elements of a row: element offset / 32)

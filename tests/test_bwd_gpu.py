@@ -79,6 +79,23 @@ def test_bwd_batch_heads(fa):
             _check_grad(host_f64(g), r, n)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_heads_in_groups_of_four_per_xcd(fa, D):
+    """B * H a multiple of 32 takes the grid order that hands each XCD four heads at a time,
+    in both backward kernels; every head and tile must still be computed once, in its place."""
+    B, H, T = 2, 16, 300
+    scale = 1.0 / math.sqrt(D)
+    for causal in (False, True):
+        print(f"case bwd grouped grid B={B} H={H} T={T} D={D} causal={causal}", flush=True)
+        d = synth.make_inputs(B, H, T, D, "bf16", seed=410 + D, with_do=True)
+        *_, dq, dk, dv = _gpu_fwd_bwd(fa, d, causal, scale)
+        q64, k64, v64, do64 = (as_f64(d[n], "bf16") for n in ("q", "k", "v", "do"))
+        o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, scale, causal)
+        ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
+        for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+            _check_grad(host_f64(g), r, n)
+
+
 def test_workload_backward_causal_t4096(fa):
     w = synth.WORKLOADS["bwd_bf16_b2h16t4096d128_causal"]
     d = synth.make_workload_inputs(w)
