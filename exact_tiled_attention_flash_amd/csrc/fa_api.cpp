@@ -47,14 +47,21 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // Query rows of one K/V head's group that one decode product holds.
 constexpr int kDecodeMaxRows = 32;
 constexpr int kDecodeKeys = 32;      // keys per decode tile
-constexpr int kDecodeTarget = 1024;  // splits x (b, K/V head) aimed at: 4 per compute unit of 256
+// Splits x (b, K/V head) aimed at: 2 workgroups per compute unit of 256 when every sequence
+// has Tk keys (measured best from 4k to 128k keys and 1 to 128 (b, K/V head)s: longer splits
+// pay each workgroup's first-load latency and the merge fewer times), 4 per compute unit when
+// lengths may differ (the splits of short sequences end early; more, shorter splits balance
+// the long ones).
+constexpr int kDecodeTargetDense = 512;
+constexpr int kDecodeTargetLens = 1024;
 
 // Split count of the decode: the caller's (clamped to the key tiles), or enough splits that
-// B * Hkv * splits is about kDecodeTarget.
-int decode_splits(int B, int Hkv, int Tk, int num_splits) {
+// B * Hkv * splits is about the target for dense or per-sequence lengths.
+int decode_splits(int B, int Hkv, int Tk, int num_splits, bool seqlens) {
   const int nt = (Tk + kDecodeKeys - 1) / kDecodeKeys;
+  const int64_t target = seqlens ? kDecodeTargetLens : kDecodeTargetDense;
   int64_t s = num_splits > 0 ? num_splits
-                             : (kDecodeTarget + int64_t(B) * Hkv - 1) / (int64_t(B) * Hkv);
+                             : (target + int64_t(B) * Hkv - 1) / (int64_t(B) * Hkv);
   if (s > nt) s = nt;
   if (s > fa::decode_max_splits()) s = fa::decode_max_splits();
   return s < 1 ? 1 : int(s);
@@ -177,7 +184,8 @@ int fa_fwd_fp8qk(const void* q8, const void* q_scale, const void* k8, const void
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, int num_splits) {
   if (check_decode(B, Hq, Hkv, Tq, Tk, D, num_splits) != FA_OK) return 0;
-  const size_t s = decode_splits(B, Hkv, Tk, num_splits);
+  // the automatic count with per-sequence lengths is never below the dense one: size for it
+  const size_t s = decode_splits(B, Hkv, Tk, num_splits, true);
   return sizeof(float) * size_t(B) * size_t(Hq) * size_t(Tq) * s * size_t(D + 4);
 }
 
@@ -195,7 +203,8 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
       !aligned16(workspace) || (cache_seqlens && !aligned4(cache_seqlens)))
     return FA_ERR_ALIGN;
   const fa::DecodeBf16Problem p{q, k, v, o, lse, cache_seqlens, workspace, B, Hq, Hkv, Tq, Tk, D,
-                                decode_splits(B, Hkv, Tk, num_splits), scale, causal != 0,
+                                decode_splits(B, Hkv, Tk, num_splits, cache_seqlens != nullptr),
+                                scale, causal != 0,
                                 static_cast<hipStream_t>(stream)};
   return fa::launch_decode_bf16(p) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -176,7 +176,8 @@ int fa_fwd_fp8qk(const void *q8, const void *q_scale, const void *k8, const void
  * num_splits (0 = the automatic choice): 4 * B * Hq * Tq * splits * (D + 4),
  * where splits is num_splits clamped to [1, min(ceil(Tk / 32), 1024)], or with
  * num_splits = 0 the smallest count that gives about 1024 (b, K/V head, split)
- * workgroups, within the same bounds. Returns 0 if the sizes are invalid.
+ * workgroups, within the same bounds (the most the automatic choice of
+ * fa_fwd_decode takes). Returns 0 if the sizes are invalid.
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D,
                                  int num_splits);
@@ -195,7 +196,10 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D,
  *   o      out: (B, Hq, Tq, D) bf16;  lse out: (B, Hq, Tq) float32
  *   workspace   at least fa_decode_workspace_bytes(...) bytes owned by the
  *               caller; partial results, contents on return unspecified
- *   num_splits  key splits per (b, K/V head); 0 = automatic (see above)
+ *   num_splits  key splits per (b, K/V head); 0 = automatic: the smallest
+ *               count that gives about 512 (b, K/V head, split) workgroups
+ *               when cache_seqlens is NULL and about 1024 when it is given,
+ *               within the bounds above
  * Causal masking is aligned at the bottom right of each sequence's valid keys
  * L: query i sees key j iff j <= i + (L - Tq). A query that sees no key gets
  * o = 0 and lse = -inf. Two kernels: the splits write their partial (max, sum,
