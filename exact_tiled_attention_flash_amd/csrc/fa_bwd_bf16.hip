@@ -18,7 +18,8 @@
 //   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key tiles up to
 //                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
-//                    read of the row-major K tile.
+//                    read of the row-major K tile. Two workgroups per compute unit (the
+//                    dK/dV kernel needs more than 256 registers a wave and runs one).
 // Tiles reach LDS by direct buffer -> LDS loads (no staging registers; rows past T arrive as
 // zeros), double-buffered and written as inline asm the compiler does not track; the
 // accumulator layout of S / S^T doubles as the B-operand layout of the following product
@@ -102,7 +103,7 @@ struct DkdvStage {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, int grp, float c,
@@ -283,8 +284,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 constexpr int kQueriesPerWG = 128;
 constexpr int kKTile = 64;
 
+// At most 256 registers a wave (the kernel fits them without spilling), so two workgroups
+// share each compute unit and each SIMD runs one wave's products under the other's vector
+// work, as in the forward; 64 KB of LDS a workgroup.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
     uint16_t* __restrict__ dQ, int T, int BH, int nq, int grp, float c, float scale) {
