@@ -59,6 +59,23 @@ def test_gqa_vs_oracle(fa, G, Tq, Tk, causal, D):
     _check(host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, f"G={G} Tq={Tq} Tk={Tk}")
 
 
+@pytest.mark.parametrize("Tq,Tk", [(150, 150), (37, 300)])
+def test_gqa_heads_in_groups_of_four_per_xcd(fa, Tq, Tk):
+    """B * (head groups) = 32: the grid order that hands each XCD four head groups at a time."""
+    B, Hkv, G, D = 4, 8, 4, 128
+    qb, kb, vb = _bf16((B, Hkv * G, Tq, D), 11), _bf16((B, Hkv, Tk, D), 12), _bf16((B, Hkv, Tk, D), 13)
+    scale = 1 / math.sqrt(D)
+    for causal in (False, True):
+        print(f"case gqa grouped grid Tq={Tq} Tk={Tk} causal={causal}", flush=True)
+        o, lse = fa.fa_fwd_gqa(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                               device_tensor(vb, "bf16"), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_forward_gqa(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                    as_f64(vb, "bf16"), scale, causal)
+        _check(host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref,
+               f"grouped Tq={Tq} Tk={Tk} causal={causal}")
+
+
 def test_gqa_single_group_equals_fa_fwd(fa):
     # one query head per K/V head and Tq == Tk: the same kernel path as fa_fwd, bit for bit
     d = synth.make_inputs(2, 4, 333, 128, "bf16", seed=5)
@@ -96,6 +113,29 @@ def test_varlen_vs_oracle(fa, G, causal, D):
                                                    as_f64(vb, "bf16"), cq, ck, scale, causal)
     # LSE is (Hq, total_q); its transpose lines up with O's (total_q, Hq) rows
     _check(host_f64(o), lse.cpu().numpy().astype(np.float64).T, o_ref, l_ref.T, "varlen")
+
+
+def test_varlen_heads_in_groups_of_four_per_xcd(fa):
+    """8 sequences x 4 heads = 32 (sequence, head) units: the grouped grid order, with empty
+    and one-row sequences among the groups."""
+    lq = [130, 0, 1, 257, 64, 65, 9, 200]
+    lk = [130, 7, 1, 257, 100, 65, 300, 200]
+    H, D = 4, 128
+    qb, cq = _pack(lq, H, D, 21)
+    kb, ck = _pack(lk, H, D, 22)
+    vb, _ = _pack(lk, H, D, 23)
+    scale = 1 / math.sqrt(D)
+    cu_q, cu_k = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    for causal in (False, True):
+        print(f"case varlen grouped grid causal={causal}", flush=True)
+        o, lse = fa.fa_fwd_varlen(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                                  device_tensor(vb, "bf16"), cu_q, cu_k, max(lq), causal=causal,
+                                  scale=scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_forward_varlen(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                       as_f64(vb, "bf16"), cq, ck, scale, causal)
+        _check(host_f64(o), lse.cpu().numpy().astype(np.float64).T, o_ref, l_ref.T,
+               f"varlen grouped causal={causal}")
 
 
 def test_varlen_equals_dense_when_lengths_match(fa):
