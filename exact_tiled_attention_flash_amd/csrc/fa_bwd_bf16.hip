@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     auto item = [&](int qb, int r) {
       const int g = r >> 2, i = r & 3;
       float pv = exp2_fast(fmaf(s[qb][r], c, -l4[qb][g][i]));
-      if (nm[qb]) {
+      if (__builtin_expect(nm[qb], 0)) {   // masked code out of line: no taken branch per score
         const int qi = q0 + 32 * qb + 8 * g + 4 * h + i;
         const bool ok = qi < T && (!CAUSAL || key <= qi);
         pv = ok ? pv : 0.f;
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = exp2_fast(fmaf(s[kb][r], c, -lse2));
-          if (need_mask) {
+          if (__builtin_expect(need_mask, 0)) {
             const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
             const bool ok = kj < T && (!CAUSAL || kj <= qrow);
             pv = ok ? pv : 0.f;
