@@ -88,6 +88,31 @@ __device__ __forceinline__ void issue_stats(uint8_t* dst, const i32x4& rsrc, int
   buf_lds_dma<4>(dst, rsrc, (uint32_t)lane * 4u, (uint32_t)min(row0, T) * 4u);
 }
 
+// Products of the D = 128 dK/dV kernel with explicit register files: S and dP in VGPRs (the
+// vector unit works on them), K and V operands and the dK, dV accumulators in AGPRs, which no
+// vector instruction touches inside the loop (left to itself the compiler parks three of the
+// eight accumulators in VGPRs and copies them through AGPRs around every product; at D = 64
+// the explicit split costs more registers than it saves moves). The compiler does not see
+// these as products, so the waits it would insert are explicit: pad() before the vector unit
+// reads a product's result or a product reads a value the vector unit just wrote.
+__device__ __forceinline__ void mfma_sv_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// 20 wait states (more than a 32x32x16 product's result latency) in program order after x's
+// last writer
+__device__ __forceinline__ void pad(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void pad_b(bf16x8& x, bf16x8& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
+}
+
 // ------------------------------------------------------------------ dK, dV
 constexpr int kKeysPerWG = 128;
 constexpr int kQTile = 64;
@@ -141,6 +166,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   for (int db = 0; db < nD; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
+  }
+  constexpr bool kAsm = D == 128;   // explicit-register products (see mfma_sv)
+  if constexpr (kAsm) {
+#pragma unroll
+    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
+#pragma unroll
+    for (int db = 0; db < nD; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
   }
 
   const int nqt = (T + kQTile - 1) / kQTile;
@@ -228,14 +261,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     for (int f = 0; f < nF; ++f) {
       const int qb = f / nK, kk = f % nK;
       if (f + 2 < nF) rd(f + 2);
-      if (kk == 0) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
+      if constexpr (kAsm) {
+        if (kk == 0) {
+          mfma_sv_first(s[qb], qa[f], kf[kk]);
+          mfma_sv_first(dp[qb], da[f], vf[kk]);
+        } else {
+          mfma_sv(s[qb], qa[f], kf[kk]);
+          mfma_sv(dp[qb], da[f], vf[kk]);
+        }
+      } else {
+        if (kk == 0) {
+          s[qb] = f32x16{};
+          dp[qb] = f32x16{};
+        }
+        s[qb] = mfma32(qa[f], kf[kk], s[qb]);
+        dp[qb] = mfma32(da[f], vf[kk], dp[qb]);
       }
-      s[qb] = mfma32(qa[f], kf[kk], s[qb]);
-      dp[qb] = mfma32(da[f], vf[kk], dp[qb]);
       __builtin_amdgcn_sched_barrier(0);
       if (f == nK / 2) stats(1);
+      if (kAsm && f == nK) pad(s[0], dp[0]);   // block 0's last products were one step back
       if (qb == 1) {
 #pragma unroll
         for (int r = (kk * 16) / nK; r < ((kk + 1) * 16) / nK; ++r) item(0, r);
@@ -259,9 +303,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     for (int t = 0; t < 2 * nT; ++t) {
       const int qb = t / nT, tt = t % nT, db = tt / 2, cc = tt % 2;
       if (t + 2 < 2 * nT) rdt(t + 2);
-      dv[db] = mfma32(ta[t], pb[qb][cc], dv[db]);
-      dk[db] = mfma32(tb[t], dsb[qb][cc], dk[db]);
+      if constexpr (kAsm) {
+        if (t == 1) pad_b(pb[0][1], dsb[0][1]);        // packed in the last S step
+        if (t == nT + 1) pad_b(pb[1][1], dsb[1][1]);   // packed one step back
+        mfma_acc(dv[db], ta[t], pb[qb][cc]);
+        mfma_acc(dk[db], tb[t], dsb[qb][cc]);
+      } else {
+        dv[db] = mfma32(ta[t], pb[qb][cc], dv[db]);
+        dk[db] = mfma32(tb[t], dsb[qb][cc], dk[db]);
+      }
       __builtin_amdgcn_sched_barrier(0);
+      if (kAsm && t == 0) pad(s[1], dp[1]);   // block 1's last products were in the last S step
       if (qb == 0) {
 #pragma unroll
         for (int r = (tt * 16) / nT; r < ((tt + 1) * 16) / nT; ++r) item(1, r);
@@ -274,6 +326,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __syncthreads();
   }
 
+  if constexpr (kAsm) {
+#pragma unroll
+    for (int db = 0; db < nD; ++db)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(dk[db]), "+a"(dv[db]));
+  }
   if (key < T) {
     store_rows_bf16<D>(dV + base + (size_t)key * D, dv, 1.0f, h);
     store_rows_bf16<D>(dK + base + (size_t)key * D, dk, scale, h);
