@@ -399,67 +399,77 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
+  // One tile's products. A causal wave computes only the tiles that start at or before its
+  // last query; the tiles after them it only helps load, in a loop of its own, so that no
+  // branch around the products makes the compiler copy the dQ accumulators at the join.
+  auto tile = [&](int j) {
     const int k0 = j * kKTile;
-    if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
     const uint8_t* Ks = smem + (j & 1) * stageBytes;
     const uint8_t* Vs = Ks + Tl::bytes;
-    if (!(CAUSAL && k0 > qw0 + 31)) {
-      f32x16 s[2], dp[2];
-      // operand fragments are read two products ahead (f = nK kb + kk)
-      constexpr int nF = 2 * nK;
-      bf16x8 ka[nF], va[nF];
+    f32x16 s[2], dp[2];
+    // operand fragments are read two products ahead (f = nK kb + kk)
+    constexpr int nF = 2 * nK;
+    bf16x8 ka[nF], va[nF];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        ka[f] = row_operand<D>(Ks, (f / nK) * 32 + l32, 2 * (f % nK) + h);
-        va[f] = row_operand<D>(Vs, (f / nK) * 32 + l32, 2 * (f % nK) + h);
-      }
-#pragma unroll
-      for (int f = 0; f < nF; ++f) {
-        const int kb = f / nK, kk = f % nK;
-        if (f + 2 < nF) {
-          ka[f + 2] = row_operand<D>(Ks, ((f + 2) / nK) * 32 + l32, 2 * ((f + 2) % nK) + h);
-          va[f + 2] = row_operand<D>(Vs, ((f + 2) / nK) * 32 + l32, 2 * ((f + 2) % nK) + h);
-        }
-        if (kk == 0) {
-          s[kb] = f32x16{};
-          dp[kb] = f32x16{};
-        }
-        s[kb] = mfma32(ka[f], qf[kk], s[kb]);
-        dp[kb] = mfma32(va[f], dof[kk], dp[kb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the first transposed K operands load under the softmax work below
-      constexpr int nT = 4 * nD;   // (db, cc), cc fastest
-      bf16x8 ta[nT];
-      ta[0] = tr_operand<D>(Ks, 0, 0, lane);
-      ta[1] = tr_operand<D>(Ks, 0, 16, lane);
-      // lane = query; register r of block kb = key k0 + 32 kb + 8*(r/4) + 4h + (r%4)
-      const bool need_mask = (k0 + kKTile > T) || (CAUSAL && (k0 + kKTile - 1 > qw0));
-      bf16x8 dsb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 ds;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2_fast(fmaf(s[kb][r], c, -lse2));
-          if (__builtin_expect(need_mask, 0)) {
-            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool ok = kj < T && (!CAUSAL || kj <= qrow);
-            pv = ok ? pv : 0.f;
-          }
-          ds[r] = pv * (dp[kb][r] - dval);
-        }
-        dsb[2 * kb] = pack8(ds, 0);
-        dsb[2 * kb + 1] = pack8(ds, 8);
-      }
-#pragma unroll
-      for (int t = 0; t < nT; ++t) {
-        if (t + 2 < nT) ta[t + 2] = tr_operand<D>(Ks, (t + 2) / 4, 16 * ((t + 2) % 4), lane);
-        dq[t / 4] = mfma32(ta[t], dsb[t % 4], dq[t / 4]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int f = 0; f < 2; ++f) {
+      ka[f] = row_operand<D>(Ks, (f / nK) * 32 + l32, 2 * (f % nK) + h);
+      va[f] = row_operand<D>(Vs, (f / nK) * 32 + l32, 2 * (f % nK) + h);
     }
+#pragma unroll
+    for (int f = 0; f < nF; ++f) {
+      const int kb = f / nK, kk = f % nK;
+      if (f + 2 < nF) {
+        ka[f + 2] = row_operand<D>(Ks, ((f + 2) / nK) * 32 + l32, 2 * ((f + 2) % nK) + h);
+        va[f + 2] = row_operand<D>(Vs, ((f + 2) / nK) * 32 + l32, 2 * ((f + 2) % nK) + h);
+      }
+      if (kk == 0) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+      }
+      s[kb] = mfma32(ka[f], qf[kk], s[kb]);
+      dp[kb] = mfma32(va[f], dof[kk], dp[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the first transposed K operands load under the softmax work below
+    constexpr int nT = 4 * nD;   // (db, cc), cc fastest
+    bf16x8 ta[nT];
+    ta[0] = tr_operand<D>(Ks, 0, 0, lane);
+    ta[1] = tr_operand<D>(Ks, 0, 16, lane);
+    // lane = query; register r of block kb = key k0 + 32 kb + 8*(r/4) + 4h + (r%4)
+    const bool need_mask = (k0 + kKTile > T) || (CAUSAL && (k0 + kKTile - 1 > qw0));
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_fast(fmaf(s[kb][r], c, -lse2));
+        if (__builtin_expect(need_mask, 0)) {
+          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool ok = kj < T && (!CAUSAL || kj <= qrow);
+          pv = ok ? pv : 0.f;
+        }
+        ds[r] = pv * (dp[kb][r] - dval);
+      }
+      dsb[2 * kb] = pack8(ds, 0);
+      dsb[2 * kb + 1] = pack8(ds, 8);
+    }
+#pragma unroll
+    for (int t = 0; t < nT; ++t) {
+      if (t + 2 < nT) ta[t + 2] = tr_operand<D>(Ks, (t + 2) / 4, 16 * ((t + 2) % 4), lane);
+      dq[t / 4] = mfma32(ta[t], dsb[t % 4], dq[t / 4]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int ntw = CAUSAL ? min(ntiles, (qw0 + 31) / kKTile + 1) : ntiles;
+  for (int j = 0; j < ntw; ++j) {
+    if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
+    tile(j);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int j = ntw; j < ntiles; ++j) {
+    if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
