@@ -18,8 +18,9 @@
 //   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key tiles up to
 //                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
-//                    read of the row-major K tile. Two workgroups per compute unit (the
-//                    dK/dV kernel needs more than 256 registers a wave and runs one).
+//                    read of the row-major K tile. Two workgroups per compute unit; the
+//                    dK/dV kernel runs two at D = 64 (239 registers a wave) and one at
+//                    D = 128 (384: K, V, dK, dV for 32 keys stay in registers).
 // Tiles reach LDS by direct buffer -> LDS loads (no staging registers; rows past T arrive as
 // zeros), double-buffered and written as inline asm the compiler does not track; the
 // accumulator layout of S / S^T doubles as the B-operand layout of the following product
@@ -127,6 +128,7 @@ struct DkdvStage {
   static_assert(bytes % 256 == 0, "stage alignment (one full pass over the LDS banks)");
 };
 
+// Two workgroups per compute unit at D = 64 (at most 256 registers a wave), one at D = 128.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
