@@ -14,6 +14,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
+SYNC_CHECK_LIB_PATH = os.path.join(_PKG, "libfa_synccheck.so")
 
 FA_F32 = 0
 FA_BF16 = 1
@@ -30,15 +31,8 @@ FA_ERR_HIP = -8
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfa.so (once) and declare the C signatures."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with "
-                          "`python exact_tiled_attention_flash_amd/build.py`")
-    lib = ctypes.CDLL(path)
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures of include/fa.h on a loaded library."""
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_abi_version.restype = i
     lib.fa_abi_version.argtypes = []
@@ -58,14 +52,32 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_fwd_decode.restype = i
     lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
-    if hasattr(lib, "fa_bwd"):
-        lib.fa_bwd.restype = i
-        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                               i, i, i, i, f, i, i, vp]
-        lib.fa_bwd_workspace_bytes.restype = sz
-        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
-    _lib = lib
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     return lib
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python exact_tiled_attention_flash_amd/build.py`")
+    _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def load_variant(path: str) -> ctypes.CDLL:
+    """Another build of the same library (the race-check build, libfa_synccheck.so), loaded
+    beside libfa.so with the same declarations; the Python wrappers keep using libfa.so."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python exact_tiled_attention_flash_amd/build.py`")
+    return _declare(ctypes.CDLL(path))
 
 
 class FaError(RuntimeError):
@@ -121,7 +133,8 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _check("out", o, q)
-    if l.dtype != torch.float32 or tuple(l.shape) != (B, H, T) or not l.is_contiguous():
+    _check_plain("lse", l, torch.float32, 3, q.device)
+    if tuple(l.shape) != (B, H, T):
         raise ValueError("lse must be a contiguous float32 (B, H, T) tensor")
     rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                     B, H, T, D, float(scale), int(bool(causal)), _dtype_code(q), _stream(q))
@@ -130,9 +143,26 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     return o, l
 
 
-def _check_plain(name: str, t: torch.Tensor, dtype: torch.dtype, dims: int):
+def _check_plain(name: str, t: torch.Tensor, dtype: torch.dtype, dims: int,
+                 device: torch.device | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or t.dim() != dims:
         raise ValueError(f"{name} must be a contiguous {dims}-d {dtype} device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, like the inputs")
+
+
+def _check_workspace(ws: torch.Tensor, need: int, device: torch.device):
+    """A caller's workspace: a contiguous device tensor on the inputs' device, of any dtype,
+    holding at least `need` bytes (the library checks the size again)."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if not ws.is_cuda or not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace must be a contiguous device tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, "
+                         f"{need} are needed")
 
 
 def fa_fwd_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
@@ -142,8 +172,9 @@ def fa_fwd_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool =
     bf16; query head h uses K/V head h // (Hq // Hkv). Causal is aligned at the bottom right.
     Returns o (B, Hq, Tq, D) and lse (B, Hq, Tq) float32. Enqueued on the current stream."""
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_plain(name, t, torch.bfloat16, 4)
+    _check_plain("q", q, torch.bfloat16, 4)
+    for name, t in (("k", k), ("v", v)):
+        _check_plain(name, t, torch.bfloat16, 4, q.device)
     if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
         raise ValueError("k and v must be (B, Hkv, Tk, D) with q's B and D")
     B, Hq, Tq, D = q.shape
@@ -152,8 +183,8 @@ def fa_fwd_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool =
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_plain("out", o, torch.bfloat16, 4)
-    _check_plain("lse", l, torch.float32, 3)
+    _check_plain("out", o, torch.bfloat16, 4, q.device)
+    _check_plain("lse", l, torch.float32, 3, q.device)
     if o.shape != q.shape or tuple(l.shape) != (B, Hq, Tq):
         raise ValueError("out must match q and lse must be (B, Hq, Tq)")
     rc = lib.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
@@ -171,10 +202,11 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
     int32 device tensors of B + 1 offsets. Returns o (total_q, Hq, D) and lse (Hq, total_q)
     float32. Enqueued on the current stream."""
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_plain(name, t, torch.bfloat16, 3)
-    _check_plain("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
-    _check_plain("cu_seqlens_k", cu_seqlens_k, torch.int32, 1)
+    _check_plain("q", q, torch.bfloat16, 3)
+    for name, t in (("k", k), ("v", v)):
+        _check_plain(name, t, torch.bfloat16, 3, q.device)
+    _check_plain("cu_seqlens_q", cu_seqlens_q, torch.int32, 1, q.device)
+    _check_plain("cu_seqlens_k", cu_seqlens_k, torch.int32, 1, q.device)
     if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
     if k.shape != v.shape or k.shape[2] != q.shape[2]:
@@ -186,8 +218,8 @@ def fa_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_plain("out", o, torch.bfloat16, 3)
-    _check_plain("lse", l, torch.float32, 2)
+    _check_plain("out", o, torch.bfloat16, 3, q.device)
+    _check_plain("lse", l, torch.float32, 2, q.device)
     if o.shape != q.shape or tuple(l.shape) != (Hq, total_q):
         raise ValueError("out must match q and lse must be (Hq, total_q)")
     rc = lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
@@ -211,8 +243,8 @@ def fa_quantize_mxfp8(x: torch.Tensor, codes: torch.Tensor | None = None,
     c = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
     s = (torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
          if scales is None else scales)
-    _check_plain("codes", c, torch.uint8, x.dim())
-    _check_plain("scales", s, torch.uint8, x.dim())
+    _check_plain("codes", c, torch.uint8, x.dim(), x.device)
+    _check_plain("scales", s, torch.uint8, x.dim(), x.device)
     if c.shape != x.shape or tuple(s.shape) != tuple(x.shape[:-1]) + (D // 32,):
         raise ValueError("codes must match x and scales must be (..., D / 32)")
     rc = lib.fa_quantize_mxfp8(x.data_ptr(), c.data_ptr(), s.data_ptr(), rows, D, FA_BF16, _stream(x))
@@ -229,22 +261,22 @@ def fa_fwd_fp8qk(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k_sc
     (B, Hq, Tq) float32. Enqueued on the current stream."""
     lib = load_library()
     _check_plain("q8", q8, torch.uint8, 4)
-    _check_plain("k8", k8, torch.uint8, 4)
-    _check_plain("v", v, torch.bfloat16, 4)
+    _check_plain("k8", k8, torch.uint8, 4, q8.device)
+    _check_plain("v", v, torch.bfloat16, 4, q8.device)
     B, Hq, Tq, D = q8.shape
     Hkv, Tk = k8.shape[1], k8.shape[2]
     if v.shape != k8.shape or k8.shape[0] != B or k8.shape[3] != D:
         raise ValueError("k8 and v must be (B, Hkv, Tk, D) with q8's B and D")
-    _check_plain("q_scale", q_scale, torch.uint8, 4)
-    _check_plain("k_scale", k_scale, torch.uint8, 4)
+    _check_plain("q_scale", q_scale, torch.uint8, 4, q8.device)
+    _check_plain("k_scale", k_scale, torch.uint8, 4, q8.device)
     if tuple(q_scale.shape) != (B, Hq, Tq, D // 32) or tuple(k_scale.shape) != (B, Hkv, Tk, D // 32):
         raise ValueError("scales must be (..., D / 32) of the codes' leading shape")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty((B, Hq, Tq, D), dtype=torch.bfloat16, device=q8.device) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q8.device) if lse is None else lse
-    _check_plain("out", o, torch.bfloat16, 4)
-    _check_plain("lse", l, torch.float32, 3)
+    _check_plain("out", o, torch.bfloat16, 4, q8.device)
+    _check_plain("lse", l, torch.float32, 3, q8.device)
     if tuple(o.shape) != (B, Hq, Tq, D) or tuple(l.shape) != (B, Hq, Tq):
         raise ValueError("out must be (B, Hq, Tq, D) and lse (B, Hq, Tq)")
     rc = lib.fa_fwd_fp8qk(q8.data_ptr(), q_scale.data_ptr(), k8.data_ptr(), k_scale.data_ptr(),
@@ -277,20 +309,21 @@ def fa_fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     B, Hq, Tq, D = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     if cache_seqlens is not None:
-        _check_plain("cache_seqlens", cache_seqlens, torch.int32, 1)
+        _check_plain("cache_seqlens", cache_seqlens, torch.int32, 1, q.device)
         if cache_seqlens.numel() != B:
             raise ValueError("cache_seqlens must hold B counts")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_plain("out", o, torch.bfloat16, 4)
-    _check_plain("lse", l, torch.float32, 3)
+    _check_plain("out", o, torch.bfloat16, 4, q.device)
+    _check_plain("lse", l, torch.float32, 3, q.device)
     if o.shape != q.shape or tuple(l.shape) != (B, Hq, Tq):
         raise ValueError("out must match q and lse must be (B, Hq, Tq)")
     need = lib.fa_decode_workspace_bytes(B, Hq, Hkv, Tq, Tk, D, int(num_splits))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     rc = lib.fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                            None if cache_seqlens is None else cache_seqlens.data_ptr(),
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -315,11 +348,13 @@ def fa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = No
     B, H, T, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+    _check_plain("lse", lse, torch.float32, 3, q.device)
+    if tuple(lse.shape) != (B, H, T):
         raise ValueError("lse must be a contiguous float32 (B, H, T) tensor")
     need = fa_bwd_workspace_bytes(B, H, T, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
@@ -328,3 +363,4 @@ def fa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = No
     if rc != FA_OK:
         raise FaError(rc)
     return dq, dk, dv
+
