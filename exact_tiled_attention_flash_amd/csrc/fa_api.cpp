@@ -81,6 +81,24 @@ int check_scale(float scale) {
 
 }  // namespace
 
+namespace fa {
+
+// Every argument of the backward except its workspace.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+              int T, int D, float scale, int causal, int dtype) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (int rc = check_sizes(B, H, T, D)) return rc;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (int rc = check_scale(scale)) return rc;
+  for (const void* p : {q, k, v, o, dout, static_cast<const void*>(lse), dq, dk, dv})
+    if (!aligned16(p)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
@@ -217,19 +235,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int T, int D) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
            int B, int H, int T, int D, float scale, int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
-  if (int rc = check_sizes(B, H, T, D)) return rc;
-  if (dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (int rc = check_scale(scale)) return rc;
+  if (int rc = fa::check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, T, D, scale, causal, dtype))
+    return rc;
+  if (!workspace) return FA_ERR_NULL;
   if (workspace_bytes < fa_bwd_workspace_bytes(B, H, T, D)) return FA_ERR_ARG;
-  for (const void* p : {q, k, v, o, dout, static_cast<const void*>(lse), static_cast<const void*>(dq),
-                        static_cast<const void*>(dk), static_cast<const void*>(dv), static_cast<const void*>(workspace)})
-    if (!aligned16(p)) return FA_ERR_ALIGN;
-
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), B, H, T, D,
                 scale, causal != 0, static_cast<hipStream_t>(stream)};
-  return fa::launch_bwd_bf16(a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a) : fa::launch_bwd_f32(a);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

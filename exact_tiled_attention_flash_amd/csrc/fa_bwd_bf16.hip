@@ -202,6 +202,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
   for (int qt = qt0; qt < nqt; ++qt) {
     const int it = qt - qt0;
+    sync_check();
     if (qt + 1 < nqt) fetch(qt + 1, smem + ((it + 1) & 1) * St::bytes);
     const uint8_t* st = smem + (it & 1) * St::bytes;
     const uint8_t* Qs = st + St::q;
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
     // dV and dK of both blocks, product t = nT qb + 2 db + cc, transposed operands read two
     // products ahead
+    sync_check();
     bf16x8 ta[2 * nT], tb[2 * nT];
     auto rdt = [&](int t) {
       const int qb = t / nT, tt = t % nT;
@@ -452,6 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     // the first transposed K operands load under the softmax work below
+    sync_check();
     constexpr int nT = 4 * nD;   // (db, cc), cc fastest
     bf16x8 ta[nT];
     ta[0] = tr_operand<D>(Ks, 0, 0, lane);
@@ -483,13 +486,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
   };
   const int ntw = CAUSAL ? min(ntiles, (qw0 + 31) / kKTile + 1) : ntiles;
+  // (each iteration of either loop passes two race-check points, so the waves of a
+  // workgroup stay in step there too)
   for (int j = 0; j < ntw; ++j) {
+    sync_check();
     if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
     tile(j);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int j = ntw; j < ntiles; ++j) {
+    sync_check();
+    sync_check();
     if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -69,6 +69,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// Race-check build (compiled with -DFA_SYNC_CHECK=1 into a separate library): every stage
+// that reads a tile from LDS is preceded by a wait for all outstanding loads and LDS accesses
+// of the wave and a workgroup barrier, so no read can overtake the direct-to-LDS loads or
+// another wave's accesses whatever the hand-placed waits do. Its results must equal the
+// release build's bit for bit. Every wave of a workgroup passes the same number of these
+// points. In the release build this is nothing.
+#ifndef FA_SYNC_CHECK
+#define FA_SYNC_CHECK 0
+#endif
+__device__ __forceinline__ void sync_check() {
+  if constexpr (FA_SYNC_CHECK != 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
 // Exchange with the lane 32 away (the other k-half of an MFMA operand).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);

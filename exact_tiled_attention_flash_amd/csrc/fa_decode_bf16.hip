@@ -213,6 +213,7 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(const DecKArgs a) {
   }
 
   auto tile = [&](auto sc, int t) __attribute__((always_inline)) {
+    sync_check();
     const uint32_t Kb = lds_addr(kslot(sc));
     const uint32_t Vb = lds_addr(vslot(sc));
     u32x4 kf[nK];

@@ -413,6 +413,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     const uint8_t* Kn = kslot_p(jp, j, 1);
     const uint8_t* Vs = vslot_p(jp, j, 0);
     pm[0] = pm[1] = kNegInf;
+    sync_check();
 
     // phase X: S of tile j+1 | key half 1 of tile j
     bf16x8 kf[QK8 ? 1 : NX];
@@ -479,6 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     });
 
     // phase Y: P V of tile j | max, reference update and key half 0 of tile j+1
+    sync_check();
     float m_old = 0.f;
     bool any = false;
     static_for<0, NY>([&](auto ic) {
@@ -516,6 +518,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
 
   // ---- last tile: finish key half 1 and multiply (no next tile) ----------------------------
   auto last = [&](auto cur, int j) {
+    sync_check();
     const uint8_t* Vs = vslot(j);
 #pragma unroll
     for (int v = 16; v < 32; ++v) exp_item(cur, v, true);
@@ -533,6 +536,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   // ---- prologue: tile 0's scores, max and key half 0 -------------------------------------
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  sync_check();
   {
     const uint8_t* K0 = kslot(0);
     if constexpr (!QK8) {

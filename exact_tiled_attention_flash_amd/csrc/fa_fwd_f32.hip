@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(
     if (more) load_kv<D>(Kh, Vh, k0 + kBlockN, T, tid, kr, vr);
     const float* Ks = smem + (j & 1) * Tl::stageElems;
     const float* Vs = Ks + Tl::tileElems;
+    sync_check();
 
     if (!(CAUSAL && k0 > qw0 + 31)) {
       f32x16 s = f32x16{};

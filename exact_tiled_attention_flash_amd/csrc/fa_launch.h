@@ -70,10 +70,15 @@ hipError_t launch_fwd_bf16(const FwdArgs &a);
 hipError_t launch_fwd_bf16_general(const FwdBf16Problem &p);
 hipError_t launch_fwd_f32(const FwdArgs &a);
 hipError_t launch_bwd_bf16(const BwdArgs &a);
+hipError_t launch_bwd_f32(const BwdArgs &a);
 hipError_t launch_decode_bf16(const DecodeBf16Problem &p);
 // Block-scaled E4M3 codes and scale bytes of `elems` bf16 values (elems a multiple of 32).
 hipError_t launch_quantize_mxfp8(const void *x, void *codes, void *scales, int64_t elems,
                                  hipStream_t stream);
 int decode_max_splits();
+// Validation of every fa_bwd argument except the workspace (status codes of include/fa.h).
+int check_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+              const float *lse, const void *dq, const void *dk, const void *dv, int B, int H,
+              int T, int D, float scale, int causal, int dtype);
 
 }  // namespace fa

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 enum fa_dtype {
     FA_F32 = 0,
@@ -217,8 +217,12 @@ int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *l
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: 8*B*H*T (the
- * row vectors D_i = rowsum(dout * o) and LSE_i * log2(e), fp32 each).
- * Returns 0 if the sizes are invalid.
+ * row vectors D_i = rowsum(dout * o) and LSE_i * log2(e), fp32 each, for
+ * either dtype). Returns 0 if the sizes are invalid.
+ * Source: "Lab 06 - Attention kernels", section 4 (the backward's O(T d)
+ * preprocessing pass computes D_i = rowsum(dO * O) once per row, so the
+ * gradient kernels read one value per query instead of reducing over P)
+ * and "Check yourself" answer 6.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int T, int D);
 
@@ -234,7 +238,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int T, int D);
  * Kernels: D_i = rowsum(dout * o); then dk, dv with key tiles outer and
  * query tiles inner; then dq with query tiles outer; P = exp(S - LSE) is
  * recomputed per tile with the same mask as the forward. No atomics: the
- * result is deterministic. Only dtype FA_BF16 is supported.
+ * result is deterministic. dtype FA_BF16: bf16 tensors, fp32 accumulation,
+ * P and dS rounded to bf16 for the matrix-core products, gradients rounded
+ * to nearest-even. dtype FA_F32: fp32 tensors, fp32 products with P and dS
+ * kept in fp32.
  * Source: "Lab 06 - Attention kernels", section 4 and the "Stretch" list
  * (two backward kernels: dK/dV with key tiles outer, dQ with query tiles
  * outer).

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -117,7 +117,8 @@ def test_bwd_validation(lib):
         assert bwd(lib, nulls=(i,)) == -1
     assert bwd(lib, T=0) == -2
     assert bwd(lib, D=32) == -3
-    assert bwd(lib, dtype=0) == -4      # the backward is bf16 only
+    assert bwd(lib, dtype=2) == -4      # FA_F32 (0) and FA_BF16 (1) only
+    assert bwd(lib, dtype=-1) == -4
     assert bwd(lib, scale=-1.0) == -6
     assert bwd(lib, causal=5) == -7
     assert bwd(lib, ws_bytes=127) == -7  # needs 8*B*H*T = 128 bytes
@@ -215,3 +216,4 @@ def test_fp8qk_validation(lib):
         assert f(nulls=(i,)) == -1
     assert f(Hq=3) == -2 and f(D=96) == -3 and f(causal=2) == -7 and f(scale=float("inf")) == -6
     assert f(mis=(0, 8)) == -5 and f(mis=(1, 2)) == -5 and f(mis=(2, 8)) == -5 and f(mis=(3, 2)) == -5
+

@@ -74,27 +74,28 @@ def test_fwd_never_reads_past_T(fa, T, causal, D, dtype):
     _check(host_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, dtype, f"T={T}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("T", [1, 65, 130])
-def test_bwd_never_reads_past_T(fa, T, causal, D):
-    print(f"case bounds bwd T={T} D={D} causal={causal}", flush=True)
-    d = synth.make_inputs(1, 1, T, D, "bf16", seed=950 + T + D, with_do=True)
-    q, k, v, do = (_dense(d, n, "bf16", T, D) for n in ("q", "k", "v", "do"))
+def test_bwd_never_reads_past_T(fa, T, causal, D, dtype):
+    print(f"case bounds bwd T={T} D={D} causal={causal} dtype={dtype}", flush=True)
+    d = synth.make_inputs(1, 1, T, D, dtype, seed=950 + T + D, with_do=True)
+    q, k, v, do = (_dense(d, n, dtype, T, D) for n in ("q", "k", "v", "do"))
     scale = 1 / math.sqrt(D)
     o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
     o = _nan_padded(o.reshape(T, D), T).view(1, 1, T, D)
     lse = _nan_padded(lse.reshape(T), T).view(1, 1, T)
     dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    q64, k64, v64, do64 = (as_f64(d[n], "bf16") for n in ("q", "k", "v", "do"))
+    q64, k64, v64, do64 = (as_f64(d[n], dtype) for n in ("q", "k", "v", "do"))
     o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, scale, causal)
     ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
     for g, r, name in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
         gh = host_f64(g)
         assert np.all(np.isfinite(gh)), name
         err = float(np.max(np.abs(gh - r)))
-        assert err <= TOL["bf16"]["grad"], f"{name} max-abs {err:.3e}"
+        assert err <= TOL[dtype]["grad"], f"{name} max-abs {err:.3e}"
 
 
 def test_varlen_never_reads_past_the_last_sequence(fa):

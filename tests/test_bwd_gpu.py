@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import as_f64, device_tensor, host_f64
+from synth import planted
+from gpu_util import as_f64, bwd_rounding_bound, device_tensor, host_f64
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -66,6 +67,81 @@ def test_bwd_sweep_vs_oracle(fa, T, causal, D):
     ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
     for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
         _check_grad(host_f64(g), r, n)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1000, 1031])
+def test_bwd_spiky_keys_vs_oracle(fa, T, causal, D):
+    # the long ragged workload's recipe at a size the oracle finishes quickly: 1 % of the key
+    # rows scaled by 8, so some rows' softmax is dominated by one key and the gradient sums
+    # cancel large terms. The bf16 roundings of O (feeding D_i) and of dS are then amplified
+    # past the flat 2e-2; each entry is held to the bound derived from those roundings
+    # (gpu_util.bwd_rounding_bound), which planted mistakes exceed (tests/test_bwd_bound.py).
+    print(f"case bwd spiky T={T} D={D} causal={causal}", flush=True)
+    d = planted.make_spiky(1, 2, T, D, seed=T + D)
+    scale = 1.0 / math.sqrt(D)
+    *_, dq, dk, dv = _gpu_fwd_bwd(fa, d, causal, scale)
+    q64, k64, v64, do64 = (as_f64(d[n], "bf16") for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, scale, causal)
+    ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
+    rep = []
+    for h in range(2):
+        bounds = bwd_rounding_bound(q64[0, h], k64[0, h], v64[0, h], do64[0, h], o_ref[0, h],
+                                    lse_ref[0, h], scale, causal)
+        for g, r, b, n in zip((dq, dk, dv), ref, bounds, ("dQ", "dK", "dV")):
+            err = np.abs(host_f64(g)[0, h] - r[0, h])
+            assert np.all(np.isfinite(err)), n
+            assert np.all(err <= b), (f"{n} head {h}: max-abs {err.max():.3e}, "
+                                      f"{int((err > b).sum())} entries over the derived bound")
+            rep.append((n, float(err.max()), float((err / b).max())))
+    print("spiky backward (grad, max-abs, largest fraction of the bound):", rep)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 7, 33, 64, 65, 129, 200, 1000])
+def test_bwd_f32_sweep_vs_oracle(fa, T, causal, D):
+    # the true-fp32 backward (fp32 products, P and dS kept in fp32) on the fp32 forward's O
+    # and LSE, element by element against the oracle at the fp32 tolerance 1e-4
+    print(f"case bwd f32 T={T} D={D} causal={causal}", flush=True)
+    d = synth.make_inputs(1, 2, T, D, "f32", seed=T * 5 + D, with_do=True)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v, do = (device_tensor(d[n], "f32") for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (as_f64(d[n], "f32") for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, scale, causal)
+    ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
+    errs = []
+    for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+        gh = host_f64(g)
+        assert np.all(np.isfinite(gh)), n
+        errs.append(float(np.max(np.abs(gh - r))))
+        assert errs[-1] <= 1e-4, f"{n} max-abs {errs[-1]:.3e}"
+    print("fp32 backward max-abs dQ, dK, dV:", errs)
+
+
+def test_bwd_f32_batch_heads_and_spiky_keys(fa):
+    # several (b, h), a ragged T, and the long workload's 1 % of keys x 8 in fp32
+    for causal in (False, True):
+        d = synth.make_inputs(2, 3, 150, 64, "f32", seed=31, with_do=True)
+        sp = planted.make_spiky(1, 2, 300, 128, seed=32)
+        for dd, dt in ((d, "f32"), ({n: as_f64(sp[n], "bf16").astype(np.float32)
+                                     for n in ("q", "k", "v", "do")}, "f32")):
+            D = dd["q"].shape[-1]
+            scale = 1.0 / math.sqrt(D)
+            q, k, v, do = (device_tensor(dd[n], dt) for n in ("q", "k", "v", "do"))
+            o, lse = fa.fa_fwd(q, k, v, causal=causal, scale=scale)
+            grads = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+            torch.cuda.synchronize()
+            q64, k64, v64, do64 = (dd[n].astype(np.float64) for n in ("q", "k", "v", "do"))
+            o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, scale, causal)
+            ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, scale, causal)
+            for g, r, n in zip(grads, ref, ("dQ", "dK", "dV")):
+                err = float(np.max(np.abs(host_f64(g) - r)))
+                assert err <= 1e-4, f"{n} D={D} causal={causal} max-abs {err:.3e}"
 
 
 def test_bwd_batch_heads(fa):
@@ -153,7 +229,7 @@ def test_bwd_argument_errors(fa):
 
     assert lib.fa_bwd_workspace_bytes(1, 1, 64, 64) == 512
     assert call(ws_bytes=511) == fa._lib.FA_ERR_ARG
-    assert call(dtype=0) == fa._lib.FA_ERR_DTYPE
+    assert call(dtype=2) == fa._lib.FA_ERR_DTYPE
     assert call(D=96) == fa._lib.FA_ERR_HEADDIM
     torch.cuda.synchronize()
     assert bool((g == 3.0).all())
