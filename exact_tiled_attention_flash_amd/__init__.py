@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     fa_abi_version,
     fa_bwd,
+    fa_bwd_noalloc,
+    fa_bwd_noalloc_max_bytes,
     fa_bwd_workspace_bytes,
     fa_decode_workspace_bytes,
     fa_fwd,

@@ -27,6 +27,7 @@ FA_ERR_ALIGN = -5
 FA_ERR_SCALE = -6
 FA_ERR_ARG = -7
 FA_ERR_HIP = -8
+FA_ERR_SCRATCH = -9
 
 _lib = None
 
@@ -56,6 +57,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    if hasattr(lib, "fa_bwd_noalloc"):
+        lib.fa_bwd_noalloc.restype = i
+        lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+        lib.fa_bwd_noalloc_max_bytes.restype = sz
+        lib.fa_bwd_noalloc_max_bytes.argtypes = []
     return lib
 
 
@@ -364,3 +370,36 @@ def fa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = No
         raise FaError(rc)
     return dq, dk, dv
 
+
+def fa_bwd_noalloc_max_bytes() -> int:
+    return load_library().fa_bwd_noalloc_max_bytes()
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+                   dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                   dv: torch.Tensor | None = None):
+    """fa_bwd without a workspace: the library's fixed scratch array holds the per-row
+    statistics. With dq, dk and dv supplied the call allocates nothing (usable under graph
+    capture). Calls that overlap on one GPU race on that array. Enqueued on the current
+    stream."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check(name, t, None if name == "q" else q)
+    B, H, T, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check_plain("lse", lse, torch.float32, 3, q.device)
+    if tuple(lse.shape) != (B, H, T):
+        raise ValueError("lse must be a contiguous float32 (B, H, T) tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, q)
+    rc = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), B, H, T, D, float(scale), int(bool(causal)),
+                            _dtype_code(q), _stream(q))
+    if rc != FA_OK:
+        raise FaError(rc)
+    return dq, dk, dv

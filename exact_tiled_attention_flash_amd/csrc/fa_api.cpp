@@ -114,6 +114,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_ARG: return "invalid argument";
     case FA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    case FA_ERR_SCRATCH: return "sizes exceed the library's fixed scratch buffer (fa_bwd_noalloc_max_bytes)";
     default: return "unknown status";
   }
 }

@@ -69,7 +69,8 @@ enum fa_status {
     FA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
     FA_ERR_SCALE = -6,     /* scale is negative, NaN or infinite */
     FA_ERR_ARG = -7,       /* any other bad argument (causal not 0/1, workspace too small) */
-    FA_ERR_HIP = -8        /* the HIP runtime rejected a launch */
+    FA_ERR_HIP = -8,       /* the HIP runtime rejected a launch */
+    FA_ERR_SCRATCH = -9    /* the sizes need more than the library's fixed scratch buffer */
 };
 
 /* Version of this ABI (FA_ABI_VERSION). */
@@ -251,6 +252,25 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            void *workspace, size_t workspace_bytes,
            int B, int H, int T, int D, float scale, int causal, int dtype,
            void *stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Arguments, results, dtypes and errors as fa_bwd, whose kernels it runs; the
+ * D_i and LSE_i * log2(e) rows live instead in a fixed device array of this library,
+ * fa_bwd_noalloc_max_bytes() bytes (16 MiB: B * H * T up to 2^21 rows), which every GPU the
+ * library runs on holds until the process ends. Sizes that need more return FA_ERR_SCRATCH
+ * and touch nothing. The array's device address is looked up once per device (on the first
+ * call with that device current); no call allocates or frees memory. Every call on one GPU
+ * uses that GPU's array: calls that overlap on one GPU (different streams, or another
+ * thread) race and must be serialised by the caller; a call may reuse the array as soon as
+ * the previous call's work has been enqueued on the same stream.
+ */
+size_t fa_bwd_noalloc_max_bytes(void);
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                   int B, int H, int T, int D, float scale, int causal, int dtype,
+                   void *stream);
 
 #ifdef __cplusplus
 }

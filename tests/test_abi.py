@@ -43,7 +43,7 @@ def test_abi_version(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert lib.fa_status_string(code)
     assert lib.fa_status_string(0) == b"ok"
     assert lib.fa_status_string(-99) == b"unknown status"
@@ -217,3 +217,17 @@ def test_fp8qk_validation(lib):
     assert f(Hq=3) == -2 and f(D=96) == -3 and f(causal=2) == -7 and f(scale=float("inf")) == -6
     assert f(mis=(0, 8)) == -5 and f(mis=(1, 2)) == -5 and f(mis=(2, 8)) == -5 and f(mis=(3, 2)) == -5
 
+
+def test_bwd_noalloc_validation(lib):
+    # every refusal happens on the host, before the runtime is touched
+    def call(T=16, D=64, dtype=1, causal=1, scale=0.1, nulls=()):
+        ptrs = [None if i in nulls else P for i in range(9)]
+        return lib.fa_bwd_noalloc(*ptrs, 1, 1, T, D, ctypes.c_float(scale), causal, dtype, None)
+    for i in range(9):
+        assert call(nulls=(i,)) == -1
+    assert call(T=0) == -2 and call(D=96) == -3 and call(dtype=2) == -4
+    assert call(causal=3) == -7 and call(scale=-1.0) == -6
+    cap = lib.fa_bwd_noalloc_max_bytes()
+    assert cap == 16 << 20
+    assert call(T=cap // 8 + 1) == -9            # one row more than the scratch array holds
+    assert lib.fa_status_string(-9).startswith(b"sizes exceed")
