@@ -45,24 +45,53 @@ def _dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def _time_launches(torch, fn, steps, warmup):
-    """Warm up, then time `steps` calls of fn() with one event pair per call on the
-    current stream (where fn enqueues its kernels). Returns (total_ms, per_call_ms)."""
+def _device_warmup(torch, fn, seconds):
+    """Run fn() untimed until `seconds` of wall time have passed (at least once): the GPU
+    leaves its idle clock over tens of milliseconds of sustained work, and a handful of warm-up
+    steps ends before that. Returns the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def _time_launches(torch, fn, steps, warmup, warm_s=0.2):
+    """Warm up, then time `steps` back-to-back calls of fn() (enqueued on the current stream)
+    between one pair of events, bracketed by device synchronisations: the whole-job rate.
+    Then time `steps` more calls with one event pair around each call: the duration of one
+    launch on its own (each event record makes the stream wait for the kernel before it, so
+    this pass has no overlap between consecutive launches and is kept out of the first).
+    Returns (total_ms of the back-to-back pass, per-launch ms list, host wall ms of the
+    back-to-back pass). Before all of it, warm_s seconds of untimed calls (_device_warmup):
+    each workload's inputs are drawn on the host while the GPU idles."""
+    if warm_s > 0:
+        _device_warmup(torch, fn, warm_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [a.elapsed_time(b) for a, b in ev]
-    total = ev[0][0].elapsed_time(ev[-1][1])
+    total = a.elapsed_time(b)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for x, y in ev:
+        x.record(stream)
+        fn()
+        y.record(stream)
+    torch.cuda.synchronize()
+    per = [x.elapsed_time(y) for x, y in ev]
     return total, per, wall_ms
 
 
@@ -80,10 +109,13 @@ def library_gemm(torch, peak):
             "tflops": round(tflops, 1), "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)}
 
 
-def _time_loop(torch, fn, steps, warmup):
-    """Warm up, then time `steps` back-to-back calls of fn() with one event pair around the
-    loop (for calls of tens of microseconds, where an event pair per call would leave gaps
-    of host time between the launches). Returns milliseconds per call."""
+def _time_loop(torch, fn, steps, warmup, warm_s=0.2):
+    """Warm up (warm_s seconds of untimed calls, then `warmup` calls), then time `steps`
+    back-to-back calls of fn() with one event pair around the loop (for calls of tens of
+    microseconds, where an event pair per call would leave gaps of host time between the
+    launches). Returns milliseconds per call."""
+    if warm_s > 0:
+        _device_warmup(torch, fn, warm_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -483,6 +515,8 @@ def main():
     ap.add_argument("--no-next-rows", action="store_true")
     ap.add_argument("--no-library-gemm", action="store_true")
     ap.add_argument("--seed", type=int, default=0, help="seed of every synthetic input")
+    ap.add_argument("--device-warmup", type=float, default=1.0,
+                    help="seconds of untimed headline steps before the W warm-up steps")
     ap.add_argument("--configs", default="1,2,4,5",
                     help="comma-separated configurations reported besides the headline (3)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -508,7 +542,8 @@ def main():
     def step():
         fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
-    total_ms, per, wall_ms = _time_launches(torch, step, args.steps, args.warmup)
+    dev_warm = _device_warmup(torch, step, args.device_warmup)
+    total_ms, per, wall_ms = _time_launches(torch, step, args.steps, args.warmup, warm_s=0)
     flops = metrics.fwd_flops(w.B, w.H, w.T, w.D, w.causal)
     ms_per_step = total_ms / args.steps
     avg_launch_ms = float(np.mean(per))
@@ -536,11 +571,18 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel": "fwd_q32_kernel<128, causal>",
                      "avg_launch_ms": round(avg_launch_ms, 5),
+                     "launch_timing": "one event pair around each of K further launches "
+                                      "(no overlap between launches)",
                      "min_launch_ms": round(float(np.min(per)), 5),
                      "median_launch_ms": round(float(np.median(per)), 5),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": metrics.fwd_bytes(w.B, w.H, w.T, w.D, 2)},
         "wall_ms_timed_region": round(wall_ms, 3),
+        "timing": "value and ms_per_step: K back-to-back steps between one event pair, "
+                  "device synchronised before and after",
+        "device_warmup": {"seconds": args.device_warmup, "steps": dev_warm,
+                          "why": "untimed steps before the W warm-up steps, so that the GPU has "
+                                 "left its idle clock when the timed region starts"},
         "device_peak": device_peak(torch),
         "context_from_pages": PAGE_CONTEXT,
     }
@@ -558,7 +600,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = COPY_BYTES
 
-    which = {c.strip() for c in args.configs.split(",") if c.strip()}
+    which = {c.strip() for c in args.configs.split(",") if c.strip() and c.strip() != "none"}
     if args.no_backward:
         which.discard("5")
     if which:

@@ -127,7 +127,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const float c = args.c;
+  // scale = 0 gives uniform weights over the visible keys; the kernel computes it as Q = 0
+  // with a positive c (every score is then exactly 0), so that c > 0 everywhere below and a
+  // masked score (-inf) always gives exp2(-inf * c - mc) = 0 with no select
+  const bool zero_scale = args.c == 0.f;
+  const float c = zero_scale ? 1.0f : args.c;
   // Workgroup -> (query tile, batch, head group) = (qt, r), hpw query heads sharing one K/V
   // head, 128 / hpw consecutive queries each; heaviest causal tile first. Within an XCD's
   // group of r the tiles walk the same keys at about the same time and share each K/V line.
@@ -225,8 +229,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   if constexpr (!QK8) {
 #pragma unroll
     for (int kk = 0; kk < nK; ++kk) {
-      u32x4 x = qrow < Tq ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
+      u32x4 x = qrow < Tq && !zero_scale
+                    ? *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * args.q_rs + kk * 16 + h * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
       qf[kk] = as_bf16x8(x);
     }
 #pragma unroll
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
 #pragma unroll
     for (int kk = 0; kk < nK8; ++kk) {
       u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-      if (qrow < Tq) {
+      if (qrow < Tq && !zero_scale) {
         x0 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 16 * h);
         x1 = *reinterpret_cast<const u32x4*>(Qr + 64 * kk + 32 + 16 * h);
       }
@@ -304,12 +309,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b2));
     pm[kb] = m;
   };
-  auto exp_item = [&](auto par, int v, bool masked) {
+  auto exp_item = [&](auto par, int v) {
     const int kb = v >> 4, rr = v & 15;
     f32x16& blk = sblk(par, kb);
     const float x = blk[rr];
+    // masked scores are -inf and mc is finite (0 while a row has seen no key), so they give 0
     float e = exp2_fast(fmaf(x, c, -mc));
-    e = (masked && x == kNegInf) ? 0.f : e;
     asm volatile("" : "+v"(e));   // keeps the exponential at its step
     blk[rr] = e;
   };
@@ -340,16 +345,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       tr[i] = 0.f;
     }
   };
-  // full-row max of the next tile; moves the references (every row of the wave, when any row
-  // exceeds its reference by more than the margin) and says whether a rescale is due
+  // moves the references (every row of the wave, when any row's next tile exceeds its
+  // reference by more than the margin) and says whether a rescale is due. A row's maximum
+  // beats the reference by the margin iff one of its two key halves (lanes l and l ^ 32) does,
+  // and the ballot covers both halves, so the decision needs no cross-half exchange; the
+  // full-row maximum is formed only when the reference moves (wave-uniform, rare after the
+  // first tile).
   auto reduce = [&](float& m_old) {
-    const float a = halves_max1(fmaxf(pm[0], pm[1]));
-    const bool need = (a - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
-    const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+    const float ah = fmaxf(pm[0], pm[1]);
     m_old = m_ref;
-    m_ref = any ? fmaxf(m_ref, a) : m_ref;
-    mc = m_ref * c;
-    return any;
+    if constexpr (D == 128) {
+      const bool need = (ah - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
+      const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+      if (__builtin_expect(any, 0)) {   // out of line: the common path falls through
+        m_ref = fmaxf(m_ref, halves_max1(ah));
+        mc = m_ref == kNegInf ? 0.f : m_ref * c;
+      }
+      return any;
+    } else {
+      // D = 64 has half the steps per tile to hide a branch in: the full-row maximum every
+      // tile, no branch (measured faster there)
+      const float a = halves_max1(ah);
+      const bool need = (a - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
+      const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
+      m_ref = any ? fmaxf(m_ref, a) : m_ref;
+      mc = m_ref == kNegInf ? 0.f : m_ref * c;
+      return any;
+    }
   };
   auto rescale = [&](float m_old) {
     const float alpha = m_old == m_ref ? 1.f : exp2_fast((m_old - m_ref) * c);
@@ -464,7 +486,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       if constexpr (i == S::XM0) fence1(sblk(nxt, 0));
       static_for<16, 32>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
-        if constexpr (S::x_exp(v) == i) exp_item(cur, v, MASK);
+        if constexpr (S::x_exp(v) == i) exp_item(cur, v);
         if constexpr (S::x_sum(v) == i) sum_item(cur, v);
       });
       static_for<2, 4>([&](auto cc_) {
@@ -497,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       if constexpr (i == S::YR) any = reduce(m_old);
       static_for<0, 16>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
-        if constexpr (S::y_exp(v) == i) exp_item(nxt, v, MASK);
+        if constexpr (S::y_exp(v) == i) exp_item(nxt, v);
         if constexpr (S::y_sum(v) == i) sum_item(nxt, v);
       });
       static_for<0, 2>([&](auto cc_) {
@@ -521,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     sync_check();
     const uint8_t* Vs = vslot(j);
 #pragma unroll
-    for (int v = 16; v < 32; ++v) exp_item(cur, v, true);
+    for (int v = 16; v < 32; ++v) exp_item(cur, v);
 #pragma unroll
     for (int v = 16; v < 32; ++v) sum_item(cur, v);
     pack_item(cur, 2);
@@ -566,9 +588,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     for (int u = 0; u < 16; ++u) max_item(Par<0>{}, u >> 3, u & 7, masked, lim);
     // a row that sees no key of tile 0 keeps -inf here; its exponentials are all masked to 0
     m_ref = halves_max1(fmaxf(pm[0], pm[1]));
-    mc = m_ref * c;
+    mc = m_ref == kNegInf ? 0.f : m_ref * c;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) exp_item(Par<0>{}, v, masked);
+    for (int v = 0; v < 16; ++v) exp_item(Par<0>{}, v);
 #pragma unroll
     for (int v = 0; v < 16; ++v) sum_item(Par<0>{}, v);
     pack_item(Par<0>{}, 0);
