@@ -9,18 +9,20 @@
 // no atomics are needed and the result is deterministic.
 //
 //   bwd_pre_kernel   D_i = sum_d dO_id O_id and LSE_i * log2(e), into the workspace (HBM-bound)
-//   bwd_dkdv_kernel  workgroup = 128 keys (32 per wave) of one (b, h); loops over 64-query
-//                    tiles from the diagonal down. Per wave: S = Q K^T and dP = dO V^T with
-//                    K, V held in registers (lane = key), then dV^T += dO^T P and
+//   bwd_dkdv_kernel  (D = 64) workgroup = 128 keys (32 per wave) of one (b, h); loops over
+//                    64-query tiles from the diagonal down. Per wave: S = Q K^T and dP = dO V^T
+//                    with K, V held in registers (lane = key), then dV^T += dO^T P and
 //                    dK^T += Q^T dS, whose A operands are transposing LDS reads of the
 //                    row-major Q and dO tiles. The tile's two 32-query blocks run as one
 //                    pipelined body: one block's exponentials under the other's products.
+//   bwd_dkdv16_kernel (D = 128) the same with 16 keys a wave on 16 x 16 x 32 products, 64 keys
+//                    a workgroup: K, V and the dK, dV accumulators of 32 keys would not leave
+//                    room for two waves on a SIMD at D = 128, those of 16 keys do.
 //   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key tiles up to
 //                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
 //                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
-//                    read of the row-major K tile. Two workgroups per compute unit; the
-//                    dK/dV kernel runs two at D = 64 (239 registers a wave) and one at
-//                    D = 128 (384: K, V, dK, dV for 32 keys stay in registers).
+//                    read of the row-major K tile. All three gradient kernels run two
+//                    workgroups per compute unit (at most 256 registers a wave).
 // Tiles reach LDS by direct buffer -> LDS loads (no staging registers; rows past T arrive as
 // zeros), double-buffered and written as inline asm the compiler does not track; the
 // accumulator layout of S / S^T doubles as the B-operand layout of the following product
@@ -89,31 +91,6 @@ __device__ __forceinline__ void issue_stats(uint8_t* dst, const i32x4& rsrc, int
   buf_lds_dma<4>(dst, rsrc, (uint32_t)lane * 4u, (uint32_t)min(row0, T) * 4u);
 }
 
-// Products of the D = 128 dK/dV kernel with explicit register files: S and dP in VGPRs (the
-// vector unit works on them), K and V operands and the dK, dV accumulators in AGPRs, which no
-// vector instruction touches inside the loop (left to itself the compiler parks three of the
-// eight accumulators in VGPRs and copies them through AGPRs around every product; at D = 64
-// the explicit split costs more registers than it saves moves). The compiler does not see
-// these as products, so the waits it would insert are explicit: pad() before the vector unit
-// reads a product's result or a product reads a value the vector unit just wrote.
-__device__ __forceinline__ void mfma_sv_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_sv(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-// 20 wait states (more than a 32x32x16 product's result latency) in program order after x's
-// last writer
-__device__ __forceinline__ void pad(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
-}
-__device__ __forceinline__ void pad_b(bf16x8& x, bf16x8& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x), "+v"(y));
-}
-
 // ------------------------------------------------------------------ dK, dV
 constexpr int kKeysPerWG = 128;
 constexpr int kQTile = 64;
@@ -128,9 +105,10 @@ struct DkdvStage {
   static_assert(bytes % 256 == 0, "stage alignment (one full pass over the LDS banks)");
 };
 
-// Two workgroups per compute unit at D = 64 (at most 256 registers a wave), one at D = 128.
+// D = 64 (D = 128 runs bwd_dkdv16_kernel below): two workgroups per compute unit, at most 256
+// registers a wave.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, int grp, float c,
@@ -169,14 +147,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     dk[db] = f32x16{};
     dv[db] = f32x16{};
   }
-  constexpr bool kAsm = D == 128;   // explicit-register products (see mfma_sv)
-  if constexpr (kAsm) {
-#pragma unroll
-    for (int kk = 0; kk < nK; ++kk) asm volatile("" : "+a"(kf[kk]), "+a"(vf[kk]));
-#pragma unroll
-    for (int db = 0; db < nD; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-  }
+  static_assert(D == 64, "D = 128 runs bwd_dkdv16_kernel");
 
   const int nqt = (T + kQTile - 1) / kQTile;
   const int qt0 = CAUSAL ? k0 / kQTile : 0;
@@ -283,25 +254,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     for (int f = 0; f < nF; ++f) {
       const int qb = f / nK, kk = f % nK;
       if (f + 2 < nF) rd(f + 2);
-      if constexpr (kAsm) {
-        if (kk == 0) {
-          mfma_sv_first(s[qb], qa[f], kf[kk]);
-          mfma_sv_first(dp[qb], da[f], vf[kk]);
-        } else {
-          mfma_sv(s[qb], qa[f], kf[kk]);
-          mfma_sv(dp[qb], da[f], vf[kk]);
-        }
-      } else {
-        if (kk == 0) {
-          s[qb] = f32x16{};
-          dp[qb] = f32x16{};
-        }
-        s[qb] = mfma32(qa[f], kf[kk], s[qb]);
-        dp[qb] = mfma32(da[f], vf[kk], dp[qb]);
+      if (kk == 0) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
       }
+      s[qb] = mfma32(qa[f], kf[kk], s[qb]);
+      dp[qb] = mfma32(da[f], vf[kk], dp[qb]);
       __builtin_amdgcn_sched_barrier(0);
       prefetch_stats(f + 2);
-      if (kAsm && f == nK) pad(s[0], dp[0]);   // block 0's last products were one step back
       if (qb == 1) {
 #pragma unroll
         for (int r = (kk * 16) / nK; r < ((kk + 1) * 16) / nK; ++r) item(0, r);
@@ -325,17 +285,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     for (int t = 0; t < 2 * nT; ++t) {
       const int qb = t / nT, tt = t % nT, db = tt / 2, cc = tt % 2;
       if (t + 2 < 2 * nT) rdt(t + 2);
-      if constexpr (kAsm) {
-        if (t == 1) pad_b(pb[0][1], dsb[0][1]);        // packed in the last S step
-        if (t == nT + 1) pad_b(pb[1][1], dsb[1][1]);   // packed one step back
-        mfma_acc(dv[db], ta[t], pb[qb][cc]);
-        mfma_acc(dk[db], tb[t], dsb[qb][cc]);
-      } else {
-        dv[db] = mfma32(ta[t], pb[qb][cc], dv[db]);
-        dk[db] = mfma32(tb[t], dsb[qb][cc], dk[db]);
-      }
+      dv[db] = mfma32(ta[t], pb[qb][cc], dv[db]);
+      dk[db] = mfma32(tb[t], dsb[qb][cc], dk[db]);
       __builtin_amdgcn_sched_barrier(0);
-      if (kAsm && t == 0) pad(s[1], dp[1]);   // block 1's last products were in the last S step
       prefetch_stats(nF + t + 2);
       if (qb == 0) {
 #pragma unroll
@@ -349,14 +301,252 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __syncthreads();
   }
 
-  if constexpr (kAsm) {
-#pragma unroll
-    for (int db = 0; db < nD; ++db)
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(dk[db]), "+a"(dv[db]));
-  }
   if (key < T) {
     store_rows_bf16<D>(dV + base + (size_t)key * D, dv, 1.0f, h);
     store_rows_bf16<D>(dK + base + (size_t)key * D, dk, scale, h);
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV with 16 keys a wave
+// D = 128: a wave owns 16 keys, so that K and V (B operands, 16 registers each) and the dK^T,
+// dV^T accumulators (8 blocks of 16 x 16, 32 registers each) leave room for two waves on every
+// SIMD (at most 256 registers a wave): one wave's softmax work runs under the other's products,
+// as in the forward and dQ kernels. Products are v_mfma_f32_16x16x32_bf16 (16 x 16 output,
+// k = 32): A lane l supplies row l % 16, B lane l column l % 16, both the 8 k-values of lane group
+// l / 16; the result's lane l holds column l % 16, rows 4 (l / 16) + i in register i.
+//   S = Q K^T and dP = dO V^T per 16-query block qb: A = 16 bytes of Q (dO) row 16 qb + l % 16,
+//     logical chunk 4 kk + l / 16 of the LDS tile; B = K (V) of key l % 16, the same 8 d-values.
+//     Result: lane = key, register i = query 16 qb + 4 (l / 16) + i.
+//   dV^T += dO^T P and dK^T += Q^T dS per 32-query chunk c: B = P (dS) of blocks 2c and 2c + 1
+//     packed to bf16, so lane group g holds queries 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3);
+//     A = the same queries of dO (Q) at column d = 16 db + l % 16, two transposing reads.
+constexpr int kKeysPerWG16 = 64;
+
+template <bool B>
+struct MaskTag {
+  static constexpr bool value = B;
+};
+template <int P>
+struct StageTag {
+  static constexpr int value = P;
+};
+
+template <int D>
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int T, int BH, int grp, float c,
+    float scale) {
+  static_assert(D == 128, "the 16-keys-a-wave schedule is laid out for D = 128");
+  using Tl = SwzTileT<D>;   // Q and dO tiles: see SwzTileT
+  using St = DkdvStage<D>;
+  constexpr int nD = D / 16;   // 16-wide d blocks of dK^T, dV^T
+  constexpr int nK = D / 32;   // k-steps of S and dP
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * St::bytes];
+
+  const int tid = lane_thread_id();
+  const int wave = wave_id();
+  const int lane = tid & 63;
+  const int j16 = lane & 15;
+  const int g = lane >> 4;
+
+  const int L = workgroup_id();
+  int bh, kt;
+  xcd_grid_item(L, BH, (T + kKeysPerWG16 - 1) / kKeysPerWG16, grp, bh, kt);
+  const int k0 = kt * kKeysPerWG16;   // key tile 0 (the heaviest when causal) first
+  const int kw0 = k0 + wave * 16;
+  const int key = kw0 + j16;
+  const size_t base = (size_t)bh * T * D;
+  const size_t rbase = (size_t)bh * T;
+
+  // B operands: K and V of this lane's key, d = 32 kk + 8 g + 0..7
+  bf16x8 kf[nK], vf[nK];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) {
+    const size_t off = base + (size_t)key * D + kk * 32 + g * 8;
+    kf[kk] = as_bf16x8(key < T ? *reinterpret_cast<const u32x4*>(K + off) : u32x4{0u, 0u, 0u, 0u});
+    vf[kk] = as_bf16x8(key < T ? *reinterpret_cast<const u32x4*>(V + off) : u32x4{0u, 0u, 0u, 0u});
+  }
+  f32x4 dk[nD], dv[nD];
+#pragma unroll
+  for (int db = 0; db < nD; ++db) {
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // per-lane LDS offsets. Row-operand reads: row 16 qb + j16, logical chunk 4 kk + g (the swizzle
+  // depends on row bits 0-3 only, so 16 qb is a constant offset). Transposing reads: lane i of
+  // group g addresses row 4 g + i / 4 (+ 32 c + 16 hi, constant offsets), columns 16 db + 4 (i % 4).
+  uint32_t roff[nK], toff[nD];
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) roff[kk] = (uint32_t)Tl::offset(j16, 4 * kk + g);
+  {
+    const int row = 4 * g + (j16 >> 2);
+#pragma unroll
+    for (int db = 0; db < nD; ++db) {
+      const int d0 = 16 * db + 4 * (j16 & 3);
+      toff[db] = (uint32_t)(Tl::offset(row, d0 >> 3) + (d0 & 7) * 2);
+    }
+  }
+  auto rowop = [&](const uint8_t* tile, int qb, int kk) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + qb * 16 * Tl::RB + roff[kk]));
+  };
+  auto trop = [&](const uint8_t* tile, int cc, int db) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint8_t* b0 = tile + cc * 32 * Tl::RB + toff[db];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b0 + 16 * Tl::RB));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  const int nqt = (T + kQTile - 1) / kQTile;
+  const int qt0 = CAUSAL ? k0 / kQTile : 0;
+  const BufTileLoader<D, Tl> ld(wave, lane);
+  const uint32_t tbytes = (uint32_t)T * (uint32_t)D * 2u;
+  const i32x4 Qr = rows_rsrc(Q + base, tbytes), dOr = rows_rsrc(dO + base, tbytes);
+  const i32x4 Lr = rows_rsrc(L2 + rbase, (uint32_t)T * 4u), Dr = rows_rsrc(Dv + rbase, (uint32_t)T * 4u);
+  auto fetch = [&](int qt, uint8_t* st) {
+    const int q0 = qt * kQTile;
+    ld.issue_all(st + St::q, Qr, q0, T);
+    ld.issue_all(st + St::dO, dOr, q0, T);
+    if (wave == 0) issue_stats(st + St::lse2, Lr, q0, T, lane);
+    if (wave == 1) issue_stats(st + St::dvec, Dr, q0, T, lane);
+  };
+
+  // One query tile. Steps are pinned with sched_barrier; operands are read two steps ahead.
+  //   phase 1, steps f = 4 qb + kk (16): S and dP products of block qb; block qb - 1's
+  //     exponentials and dS (one query row i = kk of the block per step) run under them
+  //   phase 2, steps t = 8 cc + db (16): dV and dK products of chunk cc; block 3's softmax
+  //     runs under steps 0-3 and its chunk is packed at step 4 (first used at step 8)
+  // MASK: the tile may hold a query before one of this wave's keys (causal) or past T.
+  auto tile = [&](int qt, auto par_tag, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;   // stage of this tile, known at compile time
+    sync_check();
+    // the load destination stays a run-time offset: with a constant one this toolchain emits an
+    // illegal null check on the cast of the LDS pointer inside the load helper
+    if (qt + 1 < nqt) fetch(qt + 1, smem + ((qt - qt0 + 1) & 1) * St::bytes);
+    const uint8_t* st = smem + PAR * St::bytes;
+    const uint8_t* Qs = st + St::q;
+    const uint8_t* dOs = st + St::dO;
+    const float* lse2 = reinterpret_cast<const float*>(st + St::lse2);
+    const float* dvec = reinterpret_cast<const float*>(st + St::dvec);
+    const int q0 = qt * kQTile;
+
+    f32x4 s[4], dp[4], l4[4], d4[4];
+    bf16x8 pb[2], dsb[2];
+    auto stats = [&](int qb) {
+      l4[qb] = *reinterpret_cast<const f32x4*>(lse2 + 16 * qb + 4 * g);
+      d4[qb] = *reinterpret_cast<const f32x4*>(dvec + 16 * qb + 4 * g);
+    };
+    // P = exp2(S c - LSE log2 e) and dS = P (dP - D) of row i of block qb (query
+    // q0 + 16 qb + 4 g + i), in place
+    auto item = [&](int qb, int i) {
+      float pv = exp2_fast(fmaf(s[qb][i], c, -l4[qb][i]));
+      if constexpr (MASK) {
+        const int qi = q0 + 16 * qb + 4 * g + i;
+        pv = (qi < T && (!CAUSAL || key <= qi)) ? pv : 0.f;
+      }
+      s[qb][i] = pv;
+      dp[qb][i] = pv * (dp[qb][i] - d4[qb][i]);
+    };
+    auto pack = [&](int cc) {
+      pb[cc] = as_bf16x8(u32x4{pack_bf16x2(s[2 * cc][0], s[2 * cc][1]),
+                               pack_bf16x2(s[2 * cc][2], s[2 * cc][3]),
+                               pack_bf16x2(s[2 * cc + 1][0], s[2 * cc + 1][1]),
+                               pack_bf16x2(s[2 * cc + 1][2], s[2 * cc + 1][3])});
+      dsb[cc] = as_bf16x8(u32x4{pack_bf16x2(dp[2 * cc][0], dp[2 * cc][1]),
+                                pack_bf16x2(dp[2 * cc][2], dp[2 * cc][3]),
+                                pack_bf16x2(dp[2 * cc + 1][0], dp[2 * cc + 1][1]),
+                                pack_bf16x2(dp[2 * cc + 1][2], dp[2 * cc + 1][3])});
+    };
+
+    bf16x8 qa[16], da[16];
+    auto rd1 = [&](int f) {
+      qa[f] = rowop(Qs, f / nK, f % nK);
+      da[f] = rowop(dOs, f / nK, f % nK);
+    };
+    rd1(0);
+    rd1(1);
+    stats(0);
+#pragma unroll
+    for (int f = 0; f < 4 * nK; ++f) {
+      const int qb = f / nK, kk = f % nK;
+      if (f + 2 < 4 * nK) rd1(f + 2);
+      if (kk == 0) {
+        s[qb] = mfma16<D>(qa[f], kf[kk], f32x4{0.f, 0.f, 0.f, 0.f});
+        dp[qb] = mfma16<D>(da[f], vf[kk], f32x4{0.f, 0.f, 0.f, 0.f});
+      } else {
+        s[qb] = mfma16<D>(qa[f], kf[kk], s[qb]);
+        dp[qb] = mfma16<D>(da[f], vf[kk], dp[qb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0 && qb < 3) stats(qb + 1);
+      if (qb > 0) item(qb - 1, kk);
+      if (f == 3 * nK - 1) pack(0);   // block 1's last row was just done: chunk 0 complete
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    sync_check();
+    bf16x8 ta[16], tb[16];
+    auto rd2 = [&](int t) {
+      ta[t] = trop(dOs, t / nD, t % nD);
+      tb[t] = trop(Qs, t / nD, t % nD);
+    };
+    rd2(0);
+    rd2(1);
+#pragma unroll
+    for (int t = 0; t < 2 * nD; ++t) {
+      const int cc = t / nD, db = t % nD;
+      if (t + 2 < 2 * nD) rd2(t + 2);
+      dv[db] = mfma16<D>(ta[t], pb[cc], dv[db]);
+      dk[db] = mfma16<D>(tb[t], dsb[cc], dk[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < 4) item(3, t);
+      if (t == 4) pack(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  fetch(qt0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // masked: the first tile when causal (it holds the diagonal) and a ragged last tile. Tiles
+  // go in pairs so that each one's LDS stage is a compile-time constant (the stage offsets then
+  // fold into the reads' immediate offsets).
+  const bool ragged = T % kQTile != 0;
+  auto run = [&](int qt, auto par_tag) {
+    const bool m = (CAUSAL && qt == qt0) || (ragged && qt == nqt - 1);
+    if (m) tile(qt, par_tag, MaskTag<true>{});
+    else tile(qt, par_tag, MaskTag<false>{});
+  };
+  int qt = qt0;
+  for (; qt + 1 < nqt; qt += 2) {
+    run(qt, StageTag<0>{});
+    run(qt + 1, StageTag<1>{});
+  }
+  if (qt < nqt) run(qt, StageTag<0>{});
+
+  // lane (g, j16) holds key kw0 + j16 and d = 16 db + 4 g + 0..3 of dK^T and dV^T
+  if (key < T) {
+    uint16_t* dvr = dV + base + (size_t)key * D;
+    uint16_t* dkr = dK + base + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < nD; ++db) {
+      *reinterpret_cast<u32x2*>(dvr + 16 * db + 4 * g) =
+          u32x2{pack_bf16x2(dv[db][0], dv[db][1]), pack_bf16x2(dv[db][2], dv[db][3])};
+      *reinterpret_cast<u32x2*>(dkr + 16 * db + 4 * g) =
+          u32x2{pack_bf16x2(dk[db][0] * scale, dk[db][1] * scale),
+                pack_bf16x2(dk[db][2] * scale, dk[db][3] * scale)};
+    }
   }
 }
 
@@ -522,10 +712,17 @@ hipError_t launch(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kThreads),
                      0, a.stream, o, dout, a.lse, dvec, lse2, rows);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const int nk = (a.T + kKeysPerWG - 1) / kKeysPerWG;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nk * BH), dim3(kThreads), 0, a.stream, q, k,
-                     v, dout, dvec, lse2, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv),
-                     a.T, BH, xcd_group(BH), c, a.scale);
+  if constexpr (D == 128) {
+    const int nk = (a.T + kKeysPerWG16 - 1) / kKeysPerWG16;
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<D, CAUSAL>), dim3(nk * BH), dim3(kThreads), 0, a.stream,
+                       q, k, v, dout, dvec, lse2, static_cast<uint16_t*>(a.dk),
+                       static_cast<uint16_t*>(a.dv), a.T, BH, xcd_group(BH), c, a.scale);
+  } else {
+    const int nk = (a.T + kKeysPerWG - 1) / kKeysPerWG;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nk * BH), dim3(kThreads), 0, a.stream, q,
+                       k, v, dout, dvec, lse2, static_cast<uint16_t*>(a.dk),
+                       static_cast<uint16_t*>(a.dv), a.T, BH, xcd_group(BH), c, a.scale);
+  }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   const int nq = (a.T + kQueriesPerWG - 1) / kQueriesPerWG;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream, q, k,

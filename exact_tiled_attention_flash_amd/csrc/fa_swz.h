@@ -73,6 +73,28 @@ struct SwzTile {
   }
 };
 
+// The same tile with another swizzle (D = 128), for tiles read as 16-row operands and by
+// transposing reads in which 16-lane group g (of 4) takes rows 4 g .. 4 g + 3 of an aligned 16
+// and one pair of adjacent logical chunks. Row bits 0-1 go to chunk bits 1-2, row bit 2 to
+// chunk bit 0 and (row bit 2 xor row bit 3) to chunk bit 3. Any aligned 16 rows reading one
+// logical chunk land on 16 distinct chunks; in a transposing read, groups 0 and 3 fill one
+// half of the 16 chunk positions and groups 1 and 2 the other, so whichever two groups the
+// LDS serves together, their 64 lanes hit distinct banks (64 banks).
+template <int D>
+struct SwzTileT {
+  static_assert(D == 128, "laid out for 16 chunks a row");
+  static constexpr int CH = D / 8;
+  static constexpr int RB = D * 2;
+  static constexpr int bytes = 64 * RB;
+  static constexpr int loadsPerWave = 64 * CH / 256;
+  __device__ static __forceinline__ int swz(int row) {
+    return ((row & 3) << 1) | ((row >> 2) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 3);
+  }
+  __device__ static __forceinline__ int offset(int row, int lchunk) {
+    return row * RB + ((lchunk ^ swz(row)) << 4);
+  }
+};
+
 // Direct buffer -> LDS loads of 64-row tiles of a (rows x D) matrix by the 4 waves of a
 // workgroup, through a buffer resource over the source's T rows (rows_rsrc). Lane `lane` of
 // load i of wave `wave` fills tile bytes [16 u, 16 u + 16), u = (wave * loadsPerWave + i) * 64
@@ -82,9 +104,9 @@ struct SwzTile {
 // `wave` must be wave-uniform (it selects the LDS destination); rows of the source are
 // `row_stride` elements apart (D for a (rows x D) matrix, H*D for one head of a packed
 // (rows, H, D) array), and rows up to T of one source stay below 2^31 bytes.
-template <int D>
+template <int D, class TileT = SwzTile<D>>
 struct BufTileLoader {
-  using Tl = SwzTile<D>;
+  using Tl = TileT;
   uint32_t vofs[Tl::loadsPerWave];   // byte offset of the lane's i-th chunk from the tile's row 0
   int wave;
   uint32_t rsb;                      // bytes between consecutive rows of the source matrix
