@@ -615,9 +615,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   // One tile's products. A causal wave computes only the tiles that start at or before its
   // last query; the tiles after them it only helps load, in a loop of its own, so that no
   // branch around the products makes the compiler copy the dQ accumulators at the join.
-  auto tile = [&](int j) {
+  // PAR: the tile's LDS stage as a compile-time constant (the stage offset folds into the
+  // reads' immediate offsets); MASK: the tile may hold a key after one of the wave's queries
+  // (causal) or past T, so its scores are masked.
+  auto tile = [&](int j, auto par_tag, auto mask_tag) {
+    constexpr int PAR = decltype(par_tag)::value;   // -1: stage j & 1 at run time
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = j * kKTile;
-    const uint8_t* Ks = smem + (j & 1) * stageBytes;
+    const uint8_t* Ks = smem + (PAR < 0 ? (j & 1) : PAR) * stageBytes;
     const uint8_t* Vs = Ks + Tl::bytes;
     f32x16 s[2], dp[2];
     // operand fragments are read two products ahead (f = nK kb + kk)
@@ -650,7 +655,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     ta[0] = tr_operand<D>(Ks, 0, 0, lane);
     ta[1] = tr_operand<D>(Ks, 0, 16, lane);
     // lane = query; register r of block kb = key k0 + 32 kb + 8*(r/4) + 4h + (r%4)
-    const bool need_mask = (k0 + kKTile > T) || (CAUSAL && (k0 + kKTile - 1 > qw0));
     bf16x8 dsb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -658,10 +662,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = exp2_fast(fmaf(s[kb][r], c, -lse2));
-        if (__builtin_expect(need_mask, 0)) {
+        if constexpr (MASK) {
           const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool ok = kj < T && (!CAUSAL || kj <= qrow);
-          pv = ok ? pv : 0.f;
+          pv = (kj < T && (!CAUSAL || kj <= qrow)) ? pv : 0.f;
         }
         ds[r] = pv * (dp[kb][r] - dval);
       }
@@ -676,16 +679,36 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
   };
   const int ntw = CAUSAL ? min(ntiles, (qw0 + 31) / kKTile + 1) : ntiles;
-  // (each iteration of either loop passes two race-check points, so the waves of a
-  // workgroup stay in step there too)
-  for (int j = 0; j < ntw; ++j) {
+  // tiles [0, nu) need no mask: every key at or before the wave's first query, none past T
+  const int nfull = T / kKTile;
+  const int nu = CAUSAL ? min(nfull, qw0 >= kKTile - 1 ? (qw0 - (kKTile - 1)) / kKTile + 1 : 0)
+                        : nfull;
+  // Straight-line loops only (a branch around a tile body makes the compiler copy the dQ
+  // accumulators at the join): unmasked tiles in pairs with compile-time stages, then the
+  // rest of the wave's tiles with masks and a run-time stage, then the tiles it only helps
+  // load. Each iteration of every loop passes two race-check points.
+  int j = 0;
+  for (; j + 1 < nu; j += 2) {
     sync_check();
-    if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
-    tile(j);
+    fetch(j + 1, smem + stageBytes);
+    tile(j, StageTag<0>{}, MaskTag<false>{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    sync_check();
+    // the load destination stays a run-time offset (see the dK/dV kernel)
+    if (j + 2 < ntiles) fetch(j + 2, smem + ((j + 2) & 1) * stageBytes);
+    tile(j + 1, StageTag<1>{}, MaskTag<false>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int j = ntw; j < ntiles; ++j) {
+  for (; j < ntw; ++j) {
+    sync_check();
+    if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
+    tile(j, StageTag<-1>{}, MaskTag<true>{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (; j < ntiles; ++j) {
     sync_check();
     sync_check();
     if (j + 1 < ntiles) fetch(j + 1, smem + ((j + 1) & 1) * stageBytes);
