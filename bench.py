@@ -519,6 +519,8 @@ def main():
                     help="seconds of untimed headline steps before the W warm-up steps")
     ap.add_argument("--configs", default="1,2,4,5",
                     help="comma-separated configurations reported besides the headline (3)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only configuration 5 (the backward), for the backward's profiles")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -532,6 +534,18 @@ def main():
     import exact_tiled_attention_flash_amd as fa
     import synth
     from exact_tiled_attention_flash_amd import metrics
+
+    if args.backward_only:
+        if args.calibrate_copy:
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        rows = config_rows(torch, fa, metrics, {"5"}, args.steps, args.warmup, args.seed,
+                           metrics.PEAK_TFLOPS["bf16"])
+        print(json.dumps({"backward_only": rows["5"]}))
+        return
 
     w = synth.WORKLOADS[FWD_WORKLOAD]
     d = synth.make_workload_inputs(w, seed=args.seed)
