@@ -553,6 +553,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p[2]), "+v"(p[3]));
 #pragma unroll
     for (int g = 0; g < NY; ++g) mfma_o(acc[g % nD], v_frag(Vs, g), p[g / nD]);
+    // the products are inline asm, whose latency the compiler does not see: the padding sits
+    // here, right after them, so that no register copy the compiler places where the callers'
+    // paths join can read an accumulator before its product has written it
+    fence_acc(acc);
   };
 
   // ---- prologue: tile 0's scores, max and key half 0 -------------------------------------
@@ -612,14 +616,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     ++j;
   }
   // masked tail (at most the diagonal tiles): one body, the next tile's key half 1 moved into
-  // the even buffer after each iteration so the roles never alternate
+  // the even buffer after each iteration so the roles never alternate. A wave none of whose
+  // queries sees a key of the last tile (causal: the first waves of the workgroup) stops one
+  // tile early: it finishes tile ntiles - 2 on its own, issues its share of the last tile's V
+  // loads (the other waves read them) and meets the barrier that iteration would have held.
+  const bool dead = CAUSAL && ntiles >= 2 && qw0 + 31 + shift < (ntiles - 1) * kBlockN;
   for (; j + 1 < ntiles; ++j) {
+    if (dead && j + 2 == ntiles) break;
     iteration(Par<0>{}, Par<1>{}, j, Flag<true>{}, IC<-1>{});
     s1a = s1b;
   }
-  last(Par<0>{}, j);
+  if (dead && j + 2 == ntiles) {
+#pragma unroll
+    for (int i = 0; i < Tl::loadsPerWave; ++i) ld.issue(vslot(j + 1), Vr, (j + 1) * kBlockN, T, i);
+    last(Par<0>{}, j);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  } else {
+    last(Par<0>{}, j);
+  }
 
-  fence_acc(acc);
   const float l_half = lp[0] + lp[1];
   const float r_half = rp[0] + rp[1];
   const float l_tot = l_half + swap_halves(l_half);
