@@ -626,14 +626,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     iteration(Par<0>{}, Par<1>{}, j, Flag<true>{}, IC<-1>{});
     s1a = s1b;
   }
-  if (dead && j + 2 == ntiles) {
+  // one call of the last-tile body on both paths, so that the accumulators stay in the same
+  // registers (two calls made the compiler copy them between register blocks at the join)
+  const bool early = dead && j + 2 == ntiles;
+  if (early) {
 #pragma unroll
     for (int i = 0; i < Tl::loadsPerWave; ++i) ld.issue(vslot(j + 1), Vr, (j + 1) * kBlockN, T, i);
-    last(Par<0>{}, j);
+  }
+  last(Par<0>{}, j);
+  if (early) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  } else {
-    last(Par<0>{}, j);
   }
 
   const float l_half = lp[0] + lp[1];

@@ -10,7 +10,9 @@ written it: the result is silently wrong. This test compiles each source that ho
 products to gfx950 assembly and checks that no instruction reads a product's destination
 within 19 wait states of an inline-asm product (the requirement of a 16-pass XDL product on
 CDNA3/CDNA4, the longest of the products used here). A product that reads the same registers
-as its accumulator input is exempt: the hardware chains dependent products itself.
+as its accumulator input is exempt: the hardware chains dependent products itself. The other
+direction is checked too: a vector-ALU instruction (register copies included) that writes a
+register an inline-asm product reads as an operand needs 2 wait states before that product.
 """
 import concurrent.futures as cf
 import os
@@ -23,6 +25,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc")
 WAIT_STATES = 19
+VALU_TO_MFMA_WAIT_STATES = 2
 
 _REG = re.compile(r"\b([av])\[(\d+):(\d+)\]|\b([av])(\d+)\b")
 
@@ -82,6 +85,36 @@ def find_hazards(asm_lines, wait_states=WAIT_STATES):
     return found
 
 
+def find_operand_hazards(asm_lines, wait_states=VALU_TO_MFMA_WAIT_STATES):
+    """(line of product, line of the writer, wait states between) for each vector-ALU write of
+    an inline-asm product's operand (A, B or accumulator input) too close before it. The scan
+    back stops at a label, a branch or a barrier."""
+    found = []
+    for i, line in enumerate(asm_lines):
+        ins = line.strip()
+        if not ins.startswith("v_mfma") or i == 0 or "ASMSTART" not in asm_lines[i - 1]:
+            continue
+        srcs = _regs(",".join(_operands(ins)[1:4]))
+        dist = 0
+        for k in range(i - 1, -1, -1):
+            u = asm_lines[k].strip()
+            if u.startswith((".LBB", "s_barrier", "s_cbranch", "s_branch")) or re.match(r"^_Z\S+:", u):
+                break
+            if not u or u.startswith((";", ".")):
+                continue
+            if u.startswith("s_nop"):
+                dist += int(u.split()[1]) + 1
+            else:
+                op, ops = u.split()[0], _operands(u)
+                if op.startswith("v_") and not op.startswith("v_mfma") and ops and _regs(ops[0]) & srcs:
+                    found.append((i + 1, k + 1, dist))
+                    break
+                dist += 1
+            if dist >= wait_states:
+                break
+    return found
+
+
 def test_checker_flags_early_reads():
     # the checker itself: an early copy is flagged, padded and chained reads are not
     early = ["\t;;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]",
@@ -96,6 +129,15 @@ def test_checker_flags_early_reads():
     compiler = ["\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]",
                 "\tv_accvgpr_read_b32 v2, a0"]
     assert find_hazards(compiler) == []
+
+    # a copy into the accumulator right before the product, then the same with padding
+    copy = ["\tv_accvgpr_mov_b32 a3, a19", "\ts_waitcnt lgkmcnt(0)"] + early[:3]
+    assert find_operand_hazards(copy) == [(4, 1, 1)]
+    assert find_operand_hazards(copy[:1] + ["\ts_nop 1"] + copy[1:]) == []
+    operand = ["\tv_cvt_pk_bf16_f32 v5, v8, v9"] + early[:3]
+    assert find_operand_hazards(operand) == [(3, 1, 0)]
+    unrelated = ["\tv_cvt_pk_bf16_f32 v12, v8, v9"] + early[:3]
+    assert find_operand_hazards(unrelated) == []
 
 
 @pytest.fixture(scope="module")
@@ -132,11 +174,15 @@ def test_inline_asm_products_are_padded(assembly):
     for f, lines in assembly.items():
         n_asm = sum(1 for i, l in enumerate(lines)
                     if l.strip().startswith("v_mfma") and i and "ASMSTART" in lines[i - 1])
-        hz = find_hazards(lines)
-        total += len(hz)
-        report.append(f"{f}: {n_asm} inline-asm products, {len(hz)} early reads")
+        hz, ow = find_hazards(lines), find_operand_hazards(lines)
+        total += len(hz) + len(ow)
+        report.append(f"{f}: {n_asm} inline-asm products, {len(hz)} early reads, "
+                      f"{len(ow)} late operand writes")
         for p, r, d in hz[:5]:
             report.append(f"  product at line {p}: read at line {r} after {d} wait states: "
                           f"{lines[r - 1].strip()}")
+        for p, w, d in ow[:5]:
+            report.append(f"  product at line {p}: operand written at line {w}, {d} wait states "
+                          f"before: {lines[w - 1].strip()}")
     print("\n".join(report))
     assert total == 0, "\n".join(report)
