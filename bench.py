@@ -19,7 +19,8 @@ parity against the oracle and the oracle's own time:
      heads)
 "next_rows" times the grouped-head, packed-batch, split-K decode and E4M3 Q K^T calls on their
 own workloads; "library_gemm" times the vendor library's bf16 GEMM (8192^3) in the same process
-as the dense bf16 rate reachable on this GPU at its sustained clock; "device_peak" recomputes
+as the dense bf16 rate reachable on this GPU at its sustained clock, and "library_copy" a 1 GiB
+device copy as the streaming rate reachable for the HBM-bound rows; "device_peak" recomputes
 the bf16 peak from the compute-unit count and peak clock the device reports. Prints one JSON
 line.
 """
@@ -107,6 +108,20 @@ def library_gemm(torch, peak):
     tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
     return {"op": "bf16 GEMM 8192x8192x8192 (torch.matmul -> hipBLASLt)", "ms": round(ms, 4),
             "tflops": round(tflops, 1), "pct_of_bf16_peak": round(100.0 * tflops / peak, 2)}
+
+
+def library_copy(torch):
+    """Context for the HBM-bound rows (decode): a device-to-device copy of 1 GiB through torch
+    (the runtime's copy kernel), bytes read plus bytes written per second. The published 8 TB/s
+    is the interface's peak; this is what a plain streaming kernel reaches on this GPU."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    ms = _time_loop(torch, lambda: b.copy_(a), 20, 5)
+    gbs = 2.0 * n / (ms * 1e-3) / 1e9
+    return {"op": "device-to-device copy of 1 GiB (torch copy_)", "ms": round(ms, 4),
+            "gbs_read_plus_write": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / 8000.0, 2)}
 
 
 def _time_loop(torch, fn, steps, warmup, warm_s=0.2):
@@ -629,6 +644,7 @@ def main():
 
     if not args.no_library_gemm:
         out["library_gemm"] = library_gemm(torch, peak)
+        out["library_copy"] = library_copy(torch)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = headline_oracle(w, d, o, lse)
