@@ -399,7 +399,7 @@ def config_rows(torch, fa, metrics, which, steps, warmup, seed, peak):
                      "flops_per_step": bflops,
                      "flop_count": "10*B*H*T^2*D/2 (S recompute, dP, dV, dQ, dK)",
                      "pct_of_bf16_peak": round(100.0 * bflops / (bms * 1e-3) / 1e12 / peak, 2),
-                     "kernels": "bwd_pre + bwd_dkdv + bwd_dq, one step each",
+                     "kernels": "bwd_dq (with D_i) + bwd_dkdv, one step each",
                      "parity": {"compared": "(b,h) heads 0 and 31, whole dQ, dK, dV",
                                 "max_abs_dq": errs[0], "max_abs_dk": errs[1], "max_abs_dv": errs[2],
                                 "tol": 2e-2, "pass": bool(max(errs) <= 2e-2 + 0.03125)},

@@ -1,4 +1,4 @@
-// Attention backward, bf16 storage, fp32 accumulation: three hand-written gfx950 kernels.
+// Attention backward, bf16 storage, fp32 accumulation: two hand-written gfx950 kernels.
 //
 // Method: "Lab 06 - Attention kernels", section 4: with P = exp(S - LSE) recomputed per tile
 // from the saved LSE, dV = P^T dO, dP = dO V^T, dS = P * (dP - D) where D_i = rowsum(dO * O)_i
@@ -8,7 +8,6 @@
 // accumulate in registers) and one with query tiles outer (dQ accumulates in registers), so
 // no atomics are needed and the result is deterministic.
 //
-//   bwd_pre_kernel   D_i = sum_d dO_id O_id and LSE_i * log2(e), into the workspace (HBM-bound)
 //   bwd_dkdv_kernel  (D = 64) workgroup = 128 keys (32 per wave) of one (b, h); loops over
 //                    64-query tiles from the diagonal down. Per wave: S = Q K^T and dP = dO V^T
 //                    with K, V held in registers (lane = key), then dV^T += dO^T P and
@@ -18,11 +17,14 @@
 //   bwd_dkdv16_kernel (D = 128) the same with 16 keys a wave on 16 x 16 x 32 products, 64 keys
 //                    a workgroup: K, V and the dK, dV accumulators of 32 keys would not leave
 //                    room for two waves on a SIMD at D = 128, those of 16 keys do.
-//   bwd_dq_kernel    workgroup = 128 queries (32 per wave); loops over 64-key tiles up to
-//                    the diagonal. Per wave: S^T = K Q^T and dP^T = V dO^T with Q, dO in
-//                    registers (lane = query), then dQ^T += K^T dS^T with K^T a transposing
-//                    read of the row-major K tile. All three gradient kernels run two
-//                    workgroups per compute unit (at most 256 registers a wave).
+//   bwd_dq_kernel    runs first. Workgroup = 128 queries (32 per wave); it computes its rows'
+//                    D_i = sum_d dO_id O_id and LSE_i * log2(e) from the dO it holds and one
+//                    read of O, and writes them to the workspace for the dK/dV kernel; then
+//                    loops over 64-key tiles up to the diagonal. Per wave: S^T = K Q^T and
+//                    dP^T = V dO^T with Q, dO in registers (lane = query), then
+//                    dQ^T += K^T dS^T with K^T a transposing read of the row-major K tile.
+//   All the gradient kernels run two workgroups per compute unit (at most 256 registers a
+//   wave).
 // Tiles reach LDS by direct buffer -> LDS loads (no staging registers; rows past T arrive as
 // zeros), double-buffered and written as inline asm the compiler does not track; the
 // accumulator layout of S / S^T doubles as the B-operand layout of the following product
@@ -41,32 +43,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
-}
-
-// ------------------------------------------------------------------ D_i, LSE_i * log2(e)
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const uint16_t* __restrict__ O,
-                                                           const uint16_t* __restrict__ dO,
-                                                           const float* __restrict__ LSE,
-                                                           float* __restrict__ Dv,
-                                                           float* __restrict__ L2, int64_t rows) {
-  constexpr int LPR = D / 8;             // lanes per row, one 16-byte chunk each
-  constexpr int RPB = kThreads / LPR;    // rows per workgroup
-  const int64_t row = (int64_t)workgroup_id() * RPB + lane_thread_id() / LPR;
-  const int ch = lane_thread_id() % LPR;
-  float s = 0.f;
-  if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(O + row * D + ch * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * D + ch * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s += bf16_lo(a[i]) * bf16_lo(b[i]) + bf16_hi(a[i]) * bf16_hi(b[i]);
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (ch == 0 && row < rows) {
-    Dv[row] = s;
-    L2[row] = LSE[row] * kLog2e;
-  }
 }
 
 // Store a 32 x D block held as D/32 accumulators (lane = row, registers = d).
@@ -560,8 +536,9 @@ constexpr int kKTile = 64;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ L2,
-    uint16_t* __restrict__ dQ, int T, int BH, int nq, int grp, float c, float scale) {
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ Dv, float* __restrict__ L2, uint16_t* __restrict__ dQ, int T, int BH, int nq,
+    int grp, float c, float scale) {
   using Tl = SwzTile<D>;
   constexpr int nD = D / 32;
   constexpr int nK = D / 16;
@@ -590,8 +567,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     qf[kk] = as_bf16x8(qrow < T ? *reinterpret_cast<const u32x4*>(Q + off) : u32x4{0u, 0u, 0u, 0u});
     dof[kk] = as_bf16x8(qrow < T ? *reinterpret_cast<const u32x4*>(dO + off) : u32x4{0u, 0u, 0u, 0u});
   }
-  const float lse2 = qrow < T ? L2[(size_t)bh * T + qrow] : 0.f;
-  const float dval = qrow < T ? Dv[(size_t)bh * T + qrow] : 0.f;
+  // D_i = rowsum(dO * O) over this lane's half of the row's d values plus the other half's
+  // (lane l ^ 32), and LSE_i log2 e; both go to the workspace for the dK/dV kernel, which runs
+  // after this one
+  float dsum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < nK; ++kk) {
+    const size_t off = base + (size_t)qrow * D + kk * 16 + h * 8;
+    const u32x4 ow = qrow < T ? *reinterpret_cast<const u32x4*>(O + off) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 dw = __builtin_bit_cast(u32x4, dof[kk]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dsum += bf16_lo(ow[i]) * bf16_lo(dw[i]) + bf16_hi(ow[i]) * bf16_hi(dw[i]);
+  }
+  const float dval = dsum + swap_halves(dsum);
+  const float lse2 = qrow < T ? LSE[(size_t)bh * T + qrow] * kLog2e : 0.f;
+  if (h == 0 && qrow < T) {
+    Dv[(size_t)bh * T + qrow] = dval;
+    L2[(size_t)bh * T + qrow] = lse2;
+  }
 
   f32x16 dq[nD];
 #pragma unroll
@@ -731,9 +725,11 @@ hipError_t launch(const BwdArgs& a) {
   const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
   float* dvec = a.delta;
   float* lse2 = a.delta + rows;
-  constexpr int rpb = kThreads / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kThreads),
-                     0, a.stream, o, dout, a.lse, dvec, lse2, rows);
+  // the dQ kernel first: it also writes D_i and LSE_i log2 e, which the dK/dV kernel reads
+  const int nq = (a.T + kQueriesPerWG - 1) / kQueriesPerWG;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream, q, k,
+                     v, o, dout, a.lse, dvec, lse2, static_cast<uint16_t*>(a.dq), a.T, BH, nq,
+                     xcd_group(BH), c, a.scale);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if constexpr (D == 128) {
     const int nk = (a.T + kKeysPerWG16 - 1) / kKeysPerWG16;
@@ -746,11 +742,6 @@ hipError_t launch(const BwdArgs& a) {
                        k, v, dout, dvec, lse2, static_cast<uint16_t*>(a.dk),
                        static_cast<uint16_t*>(a.dv), a.T, BH, xcd_group(BH), c, a.scale);
   }
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  const int nq = (a.T + kQueriesPerWG - 1) / kQueriesPerWG;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nq * BH), dim3(kThreads), 0, a.stream, q, k,
-                     v, dout, dvec, lse2, static_cast<uint16_t*>(a.dq), a.T, BH, nq, xcd_group(BH), c,
-                     a.scale);
   return hipGetLastError();
 }
 

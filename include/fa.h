@@ -236,9 +236,11 @@ size_t fa_bwd_workspace_bytes(int B, int H, int T, int D);
  *   dq, dk, dv  out: (B, H, T, D) of dtype
  *   workspace   scratch of at least fa_bwd_workspace_bytes(B, H, T, D)
  *               bytes, owned by the caller; contents on return unspecified
- * Kernels: D_i = rowsum(dout * o); then dk, dv with key tiles outer and
- * query tiles inner; then dq with query tiles outer; P = exp(S - LSE) is
- * recomputed per tile with the same mask as the forward. No atomics: the
+ * Kernels (FA_BF16): dq with query tiles outer, which also computes its rows'
+ * D_i = rowsum(dout * o) into the workspace; then dk, dv with key tiles outer
+ * and query tiles inner. FA_F32: a D_i pass, then dk, dv, then dq. P =
+ * exp(S - LSE) is recomputed per tile with the same mask as the forward. No
+ * atomics: the
  * result is deterministic. dtype FA_BF16: bf16 tensors, fp32 accumulation,
  * P and dS rounded to bf16 for the matrix-core products, gradients rounded
  * to nearest-even. dtype FA_F32: fp32 tensors, fp32 products with P and dS
