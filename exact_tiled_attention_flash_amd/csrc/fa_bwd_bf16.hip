@@ -653,13 +653,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 ds;
+      // key kj = k0 + 32 kb + 4 h + e(r), e(r) = 8 (r / 4) + r % 4, is visible iff kj < T and
+      // (causal) kj <= qrow: one compare of the constant e(r) with a per-lane limit
+      const int elim = (CAUSAL ? min(qrow, T - 1) : T - 1) - (k0 + 32 * kb + 4 * h);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = exp2_fast(fmaf(s[kb][r], c, -lse2));
-        if constexpr (MASK) {
-          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          pv = (kj < T && (!CAUSAL || kj <= qrow)) ? pv : 0.f;
-        }
+        if constexpr (MASK) pv = (8 * (r >> 2) + (r & 3)) <= elim ? pv : 0.f;
         ds[r] = pv * (dp[kb][r] - dval);
       }
       dsb[2 * kb] = pack8(ds, 0);
