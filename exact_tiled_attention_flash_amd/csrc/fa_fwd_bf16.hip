@@ -66,6 +66,14 @@ constexpr int kBlockM = 128;   // queries per workgroup, 32 per wave
 __device__ __forceinline__ void fence1(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(x));
 }
+// The same ordering point with only N + 1 wait states of padding (N = -1: none), where the
+// schedule already places that many instructions after the product: the vector reads of x
+// cannot move above it. The assembly check of the build verifies the total.
+template <int N>
+__device__ __forceinline__ void fence_n(f32x16& x) {
+  if constexpr (N < 0) asm volatile("" : "+v"(x));
+  else asm volatile("s_nop %1" : "+v"(x) : "i"(N));
+}
 
 // ---- per-step work assignment (all compile-time) --------------------------------------
 // Items of one tile: 32 score elements per lane, v = 16 kb + r; 4 chunks of 8 (v / 8 = ch,
@@ -110,6 +118,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   using Tl = SwzTile<D>;
   using Tl8 = SwzTile8<D>;
   using S = Sched1<D>;
+  // padding before the max reads of the next tile's scores: in phase X they come three steps
+  // (three products and their vector work) after the last product of key half 0, enough on
+  // their own; in phase Y two products after the last one of key half 1, which needs 8 more
+  constexpr int FX = -1, FY = 7;
   constexpr int nD = D / 32;      // 32-row blocks of O^T
   constexpr int nK = D / 16;      // k-steps of S^T = K Q^T (bf16)
   constexpr int nK8 = D / 64;     // k-steps of the E4M3 products
@@ -483,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       }
       // the step's VALU work follows its product, so consecutive products are evenly spaced
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i == S::XM0) fence1(sblk(nxt, 0));
+      if constexpr (i == S::XM0) fence_n<FX>(sblk(nxt, 0));
       static_for<16, 32>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
         if constexpr (S::x_exp(v) == i) exp_item(cur, v);
@@ -511,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       if constexpr (i + 2 < NY) vf[i + 2] = v_frag(Vs, i + 2);
       mfma_o(acc[db], vf[i], p[cc]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i == S::YM0) fence1(sblk(nxt, 1));
+      if constexpr (i == S::YM0) fence_n<FY>(sblk(nxt, 1));
       static_for<0, 8>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         if constexpr (S::y_max(t) == i) max_item(nxt, 1, t, MASK, lim);
