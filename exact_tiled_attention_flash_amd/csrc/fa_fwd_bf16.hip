@@ -367,7 +367,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     const float ah = fmaxf(pm[0], pm[1]);
     m_old = m_ref;
     if constexpr (D == 128) {
-      const bool need = (ah - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
+      // a row that has seen no key yet (m_ref = -inf) needs the move as soon as it sees one
+      // (ah finite: the difference is +inf); while it still sees none (ah = -inf too) it has
+      // nothing to move, and the comparison of the undefined difference is false
+      const bool need = (ah - m_ref) * c > kRescaleLog2;
       const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
       if (__builtin_expect(any, 0)) {   // out of line: the common path falls through
         m_ref = fmaxf(m_ref, halves_max1(ah));
