@@ -75,6 +75,29 @@ __device__ __forceinline__ void fence_n(f32x16& x) {
   else asm volatile("s_nop %1" : "+v"(x) : "i"(N));
 }
 
+// m = max(m, v[0], v[1], ..., v[2C - 1]) as C dependent v_max3_f32 in one asm statement: the
+// compiler pads the reader of an inline-asm result as if the asm were a transcendental, so a
+// chain of one-instruction statements costs a wait state per link, one statement does not
+template <int C>
+__device__ __forceinline__ void max3_chain(float& m, const float* v) {
+  static_assert(C >= 1 && C <= 4, "one to four links");
+  if constexpr (C == 1)
+    asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(v[0]), "v"(v[1]));
+  else if constexpr (C == 2)
+    asm volatile("v_max3_f32 %0, %0, %1, %2\n\tv_max3_f32 %0, %0, %3, %4"
+                 : "+v"(m) : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  else if constexpr (C == 3)
+    asm volatile("v_max3_f32 %0, %0, %1, %2\n\tv_max3_f32 %0, %0, %3, %4\n\t"
+                 "v_max3_f32 %0, %0, %5, %6"
+                 : "+v"(m) : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]));
+  else
+    asm volatile("v_max3_f32 %0, %0, %1, %2\n\tv_max3_f32 %0, %0, %3, %4\n\t"
+                 "v_max3_f32 %0, %0, %5, %6\n\tv_max3_f32 %0, %0, %7, %8"
+                 : "+v"(m)
+                 : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]),
+                   "v"(v[7]));
+}
+
 // ---- per-step work assignment (all compile-time) --------------------------------------
 // Items of one tile: 32 score elements per lane, v = 16 kb + r; 4 chunks of 8 (v / 8 = ch,
 // the B operand P[ch] of keys 16 ch .. 16 ch + 15); 8 max items per key half (pairs of
@@ -95,6 +118,17 @@ struct Sched1 {
   static constexpr int XF = (x_sum(31) > x_pack(3) ? x_sum(31) : x_pack(3)) + 1;
   static constexpr int x_max(int t) { return win_step(t, 8, XM0, XM1); }           // kb = 0
   static constexpr int y_max(int t) { return win_step(t, 8, YM0, YM1); }           // kb = 1
+  // the max items of a step are consecutive: the first one and how many
+  static constexpr int max_first(bool y, int i) {
+    for (int t = 0; t < 8; ++t)
+      if ((y ? y_max(t) : x_max(t)) == i) return t;
+    return 0;
+  }
+  static constexpr int max_count(bool y, int i) {
+    int n = 0;
+    for (int t = 0; t < 8; ++t) n += (y ? y_max(t) : x_max(t)) == i;
+    return n;
+  }
   static constexpr int y_exp(int v) { return win_step(v, 16, YE0, YE1); }          // v in [0, 16)
   static constexpr int y_sum(int v) { return win_step(v, 16, YS0, YS1); }
   // chunk ch (0, 1) of the next tile overwrites P[ch] one step after this tile's last product
@@ -321,6 +355,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(a), "v"(b2));
     pm[kb] = m;
   };
+  // max items t0 .. t0 + n - 1 of key half kb (masks as in max_item), chained in statements of
+  // up to four links
+  auto max_items = [&](auto par, int kb, auto t0c, auto nc, bool masked, int lim) {
+    constexpr int t0 = decltype(t0c)::value, n = decltype(nc)::value;
+    f32x16& x = sblk(par, kb);
+    float v[2 * n];
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+      const int t = t0 + k;
+      float a = x[2 * t], b2 = x[2 * t + 1];
+      if (masked) {
+        const int kla = 32 * kb + 8 * (t >> 1) + 2 * (t & 1);
+        a = kla < lim ? a : kNegInf;
+        b2 = kla + 1 < lim ? b2 : kNegInf;
+        x[2 * t] = a;
+        x[2 * t + 1] = b2;
+      }
+      v[2 * k] = a;
+      v[2 * k + 1] = b2;
+    }
+    float m = pm[kb];
+    static_for<0, (n + 3) / 4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      max3_chain<(n - 4 * g < 4 ? n - 4 * g : 4)>(m, v + 8 * g);
+    });
+    pm[kb] = m;
+  };
   auto exp_item = [&](auto par, int v) {
     const int kb = v >> 4, rr = v & 15;
     f32x16& blk = sblk(par, kb);
@@ -509,10 +570,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
         if constexpr (S::x_pack(ch) == i) pack_item(cur, ch);
       });
       if constexpr (i == S::XF) fold();
-      static_for<0, 8>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        if constexpr (S::x_max(t) == i) max_item(nxt, 0, t, MASK, lim);
-      });
+      if constexpr (S::max_count(false, i) > 0)
+        max_items(nxt, 0, IC<S::max_first(false, i)>{}, IC<S::max_count(false, i)>{}, MASK, lim);
       __builtin_amdgcn_sched_barrier(0);
     });
 
@@ -527,10 +586,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       mfma_o(acc[db], vf[i], p[cc]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (i == S::YM0) fence_n<FY>(sblk(nxt, 1));
-      static_for<0, 8>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        if constexpr (S::y_max(t) == i) max_item(nxt, 1, t, MASK, lim);
-      });
+      if constexpr (S::max_count(true, i) > 0)
+        max_items(nxt, 1, IC<S::max_first(true, i)>{}, IC<S::max_count(true, i)>{}, MASK, lim);
       if constexpr (i == S::YR) any = reduce(m_old);
       static_for<0, 16>([&](auto vc) {
         constexpr int v = decltype(vc)::value;
