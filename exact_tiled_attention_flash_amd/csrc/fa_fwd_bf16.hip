@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       // D = 64 has half the steps per tile to hide a branch in: the full-row maximum every
       // tile, no branch (measured faster there)
       const float a = halves_max1(ah);
-      const bool need = (a - m_ref) * c > kRescaleLog2 || m_ref == kNegInf;
+      const bool need = (a - m_ref) * c > kRescaleLog2;   // no-key rows: as for D = 128
       const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
       m_ref = any ? fmaxf(m_ref, a) : m_ref;
       mc = m_ref == kNegInf ? 0.f : m_ref * c;
