@@ -183,8 +183,9 @@ def test_workload_backward_causal_t4096(fa):
     sum_do = do.float().sum(dim=2)
     assert (sum_dv - sum_do).abs().max().item() < 0.5
     assert dk.float().sum(dim=2).abs().max().item() < 0.5
+    # and every head whole against the oracle
     report = []
-    for idx in (0, 17, 31):
+    for idx in range(w.B * w.H):
         b, h = divmod(idx, w.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         q64, k64, v64, do64 = (as_f64(d[n][sl], "bf16") for n in ("q", "k", "v", "do"))
@@ -192,7 +193,8 @@ def test_workload_backward_causal_t4096(fa):
         ref = oracle.attention_backward(q64, k64, v64, o_ref, do64, lse_ref, w.scale, True)
         for g, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
             report.append((idx, n) + _check_grad(host_f64(g[sl]), r, f"head {idx} {n}"))
-    print("B=2 H=16 T=4096 D=128 causal backward (head, grad, max-abs, entries>=8):", report)
+    worst = {n: max(r[2] for r in report if r[1] == n) for n in ("dQ", "dK", "dV")}
+    print("B=2 H=16 T=4096 D=128 causal backward, worst max-abs over every head:", worst)
 
 
 def test_bwd_deterministic(fa):
