@@ -144,6 +144,25 @@ def test_workload_long_ragged_spiky(fa):
     print("B=1 H=32 T=16381 D=128 causal spiky, worst max-abs O, LSE over every head:", worst)
 
 
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_million_key_sequence(fa, D, causal):
+    # one head of T = 2^20 + 3 (16385 key tiles, ragged): the long end of the sizes the calls
+    # accept (a head stays below 2^31 bytes up to T = 2^22 at D = 128); every tile's online
+    # rescale and the fp32 row sums over a million keys, on sampled rows including the last
+    T = (1 << 20) + 3
+    print(f"case one head T={T} D={D} causal={causal}", flush=True)
+    d = synth.make_inputs(1, 1, T, D, "bf16", seed=D + 11)
+    scale = 1 / math.sqrt(D)
+    o, lse = _run(fa, d, "bf16", causal, scale)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, T // 2, T - 3, T - 2, T - 1],
+                                     rng.integers(0, T, 6)]))
+    q, k, v = (as_f64(d[n][0, 0], "bf16") for n in "qkv")
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, scale, causal, rows)
+    e = _compare(o[0, 0, rows], lse[0, 0, rows], o_ref, lse_ref, "bf16", f"T={T} rows")
+    print(f"T={T} D={D} causal={causal} max-abs O, LSE on {len(rows)} rows:", e)
+
+
 # ------------------------------------------------------------ oracle-free properties
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
