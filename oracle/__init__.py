@@ -5,6 +5,8 @@ this package. The product (the HIP library and its binding) never does.
 """
 from .attention import (  # noqa: F401
     attention_backward,
+    attention_backward_key_tail,
+    attention_backward_rows,
     attention_cross,
     attention_decode,
     attention_forward,

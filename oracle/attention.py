@@ -208,6 +208,46 @@ def backward_delta(o, do):
     return np.sum(o * do, axis=-1)
 
 
+def attention_backward_rows(q_bh, k_bh, v_bh, do_bh, scale: float, causal: bool,
+                            rows: np.ndarray):
+    """dQ of selected query rows of one (b, h), by the definition.
+
+    [Lab06] section 4 restricted to rows i: dQ_i = scale * sum_j dS_ij K_j with
+    dS_ij = P_ij (dP_ij - D_i), P_i the softmax of row i of S, dP_i = dO_i V^T and
+    D_i = dO_i . O_i. Every quantity of row i needs row i of S only, so long
+    sequences can be checked on a sample of rows. Returns (len(rows), D) float64.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    o_r, lse_r = attention_rows(q_bh, k_bh, v_bh, scale, causal, rows)
+    s = scores(q_bh, k_bh, scale, causal, rows)
+    p = np.exp(s - lse_r[:, None])
+    dp = do_bh[rows] @ v_bh.T
+    dvec = np.sum(do_bh[rows] * o_r, axis=1)
+    ds = p * (dp - dvec[:, None])
+    return scale * (ds @ k_bh)
+
+
+def attention_backward_key_tail(q_bh, k_bh, v_bh, do_bh, scale: float, r0: int):
+    """Causal: dK and dV of keys r0 .. T-1 of one (b, h), by the definition.
+
+    Under the causal rule key j is seen only by queries i >= j, so the gradients
+    of the keys from r0 on need P, dP and D of query rows r0 .. T-1 only
+    ([Lab06] section 4: dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i);
+    each of those rows' LSE and O still comes from its whole row of S.
+    Returns (dK, dV), each (T - r0, D) float64.
+    """
+    T = k_bh.shape[0]
+    rows = np.arange(r0, T)
+    o_r, lse_r = attention_rows(q_bh, k_bh, v_bh, scale, True, rows)
+    s = scores(q_bh, k_bh, scale, True, rows)[:, r0:]
+    p = np.exp(s - lse_r[:, None])
+    dv = p.T @ do_bh[rows]
+    dp = do_bh[rows] @ v_bh[r0:].T
+    dvec = np.sum(do_bh[rows] * o_r, axis=1)
+    ds = p * (dp - dvec[:, None])
+    return scale * (ds.T @ q_bh[rows]), dv
+
+
 def attention_cross(q_h, k_h, v_h, scale: float, causal: bool):
     """One head with Tq query rows against Tk key rows: (O, LSE) in float64.
 

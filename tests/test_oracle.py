@@ -265,6 +265,34 @@ def test_backward_matches_torch_autograd(causal):
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_rows_match_torch_autograd(causal):
+    # dQ of a sample of rows, for sequences too long for the dense backward
+    shape = (1, 1, 53, 16)
+    q, k, v, do = (_rand(shape, seed=300 + i) for i in range(4))
+    scale = 0.3
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    to = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    to.backward(torch.from_numpy(do))
+    rows = np.array([0, 1, 17, 52])
+    dq = oracle.attention_backward_rows(q[0, 0], k[0, 0], v[0, 0], do[0, 0], scale, causal, rows)
+    np.testing.assert_allclose(dq, tq.grad.numpy()[0, 0, rows], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("r0", [0, 1, 30, 52])
+def test_backward_key_tail_matches_torch_autograd(r0):
+    # causal dK, dV of the keys from r0 on, from the query rows that see them
+    shape = (1, 1, 53, 16)
+    q, k, v, do = (_rand(shape, seed=310 + i) for i in range(4))
+    scale = 0.3
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+    to = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+    to.backward(torch.from_numpy(do))
+    dk, dv = oracle.attention_backward_key_tail(q[0, 0], k[0, 0], v[0, 0], do[0, 0], scale, r0)
+    np.testing.assert_allclose(dk, tk.grad.numpy()[0, 0, r0:], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv, tv.grad.numpy()[0, 0, r0:], atol=1e-12, rtol=0)
+
+
 def test_backward_delta_identity():
     # sum_j P_ij dP_ij == rowsum(dO * O)  (Lab 06 section 4)
     shape = (1, 1, 33, 8)
