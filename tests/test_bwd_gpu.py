@@ -197,6 +197,36 @@ def test_workload_backward_causal_t4096(fa):
     print("B=2 H=16 T=4096 D=128 causal backward, worst max-abs over every head:", worst)
 
 
+def test_bwd_million_key_sequence(fa):
+    # one head of T = 2^20 + 3 (ragged), D = 128, causal: dQ of sampled rows (the first, the
+    # last, the middle and random ones) and dK, dV of the last 80 keys against the oracle's
+    # restricted backward, and the two gradient sums over every key
+    T, D = (1 << 20) + 3, 128
+    print(f"case backward one head T={T} D={D} causal", flush=True)
+    d = synth.make_inputs(1, 1, T, D, "bf16", seed=41, with_do=True)
+    scale = 1 / math.sqrt(D)
+    q, k, v, do, o, lse, dq, dk, dv = _gpu_fwd_bwd(fa, d, True, scale)
+    assert (dv.float().sum(dim=2) - do.float().sum(dim=2)).abs().max().item() < 0.5
+    assert dk.float().sum(dim=2).abs().max().item() < 0.5
+    q64, k64, v64, do64 = (as_f64(d[n][0, 0], "bf16") for n in ("q", "k", "v", "do"))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, T // 2, T - 3, T - 2, T - 1],
+                                     rng.integers(0, T, 8)]))
+    ref = oracle.attention_backward_rows(q64, k64, v64, do64, scale, True, rows)
+    e_q = _check_grad(host_f64(dq)[0, 0, rows], ref, f"dQ rows of T={T}")
+    r0 = T - 80
+    ref_k, ref_v = oracle.attention_backward_key_tail(q64, k64, v64, do64, scale, r0)
+    e_k = _check_grad(host_f64(dk)[0, 0, r0:], ref_k, f"dK of the last keys of T={T}")
+    e_v = _check_grad(host_f64(dv)[0, 0, r0:], ref_v, f"dV of the last keys of T={T}")
+    # the last keys are seen by few queries of a million-key softmax: their gradients are small,
+    # so the absolute tolerance says little; they must also hold to 2^-6 of their own magnitude
+    # (bf16 rounding of P, dS and the output is 2^-9 each)
+    for e, r, n in ((e_k, ref_k, "dK"), (e_v, ref_v, "dV")):
+        assert e[0] <= 2.0 ** -6 * np.abs(r).max(), f"{n} tail: {e[0]:.3e} vs |ref| {np.abs(r).max():.3e}"
+    print(f"T={T} max-abs dQ rows, dK tail, dV tail:", e_q[0], e_k[0], e_v[0],
+          "| largest |dK|, |dV| in the tail:", np.abs(ref_k).max(), np.abs(ref_v).max())
+
+
 def test_bwd_deterministic(fa):
     d = synth.make_inputs(1, 4, 700, 128, "bf16", seed=22, with_do=True)
     r1 = _gpu_fwd_bwd(fa, d, True, 0.09)
