@@ -47,7 +47,11 @@
 //     products while the VALU takes the max over key half 1 of tile j+1, moves the
 //     references and works through key half 0 of tile j+1. Each step of a phase holds one
 //     product followed by a fixed share of the VALU work, fenced with sched_barrier. The
-//     E4M3 products (4 a tile for D = 128) sit on every fourth step of the same schedule.
+//     E4M3 products (4 a tile for D = 128, each four times the work of a bf16 one) sit on
+//     every fourth step of the same schedule; at D = 128 the first six P V products of tile j
+//     (key half 0's chunks, finished in the previous phase Y) move into phase X, on two of the
+//     three steps between E4M3 products, so phase X is not left with a quarter of the products
+//     under all of its VALU work.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -103,11 +107,22 @@ __device__ __forceinline__ void max3_chain(float& m, const float* v) {
 // the B operand P[ch] of keys 16 ch .. 16 ch + 15); 8 max items per key half (pairs of
 // elements). Key half 0 of a tile is finished in phase Y of the iteration before the one
 // that multiplies it, key half 1 in phase X of that iteration.
-template <int D>
+template <int D, int NPX = 0>
 struct Sched1 {
   static constexpr int nK = D / 16, nD = D / 32;
   static constexpr int NX = 2 * nK;   // phase X steps (S products, f = nK kb + kk)
-  static constexpr int NY = 4 * nD;   // phase Y steps (P V products, g = nD cc + db)
+  // the first NPX P V products of a tile (g = 0 .. NPX - 1, key half 0's chunks) run in phase
+  // X, on the steps i with i % 4 = 2 or 3 (the E4M3 S products take the steps i % 4 = 0)
+  static constexpr int NY = 4 * nD - NPX;   // phase Y steps (P V products g = NPX + i)
+  static constexpr int pvx(int i) {
+    int k = 0;
+    for (int t = 0; t < NX; ++t)
+      if (t % 4 >= 2 && k < NPX) {
+        if (t == i) return k;
+        ++k;
+      }
+    return -1;
+  }
   static constexpr int XE0 = 0, XE1 = NX - 3, XS0 = 1, XS1 = NX - 1;
   static constexpr int XM0 = nK + 2, XM1 = NX;
   static constexpr int YM0 = 2, YM1 = 3, YR = YM1, YE0 = YR + 1, YE1 = NY - 1;
@@ -132,9 +147,10 @@ struct Sched1 {
   static constexpr int y_exp(int v) { return win_step(v, 16, YE0, YE1); }          // v in [0, 16)
   static constexpr int y_sum(int v) { return win_step(v, 16, YS0, YS1); }
   // chunk ch (0, 1) of the next tile overwrites P[ch] one step after this tile's last product
-  // that reads it (steps nD ch .. nD ch + nD - 1)
+  // that reads it (g = nD ch + nD - 1, phase Y step g - NPX; none in Y when g < NPX)
   static constexpr int y_pack(int ch) {
-    return y_exp(8 * ch + 7) + 1 > nD * (ch + 1) + 1 ? y_exp(8 * ch + 7) + 1 : nD * (ch + 1) + 1;
+    return y_exp(8 * ch + 7) + 1 > nD * (ch + 1) + 1 - NPX ? y_exp(8 * ch + 7) + 1
+                                                            : nD * (ch + 1) + 1 - NPX;
   }
   static constexpr bool valid() {
     for (int v = 0; v < 16; ++v)
@@ -145,13 +161,18 @@ struct Sched1 {
            XM0 > nK && x_max(7) < NX;
   }
 };
-static_assert(Sched1<128>::valid() && Sched1<64>::valid(), "pipeline schedule order");
+static_assert(Sched1<128>::valid() && Sched1<64>::valid() && Sched1<128, 6>::valid(),
+              "pipeline schedule order");
+static_assert(Sched1<128, 6>::pvx(2) == 0 && Sched1<128, 6>::pvx(11) == 5 &&
+              Sched1<128, 6>::pvx(14) == -1 && Sched1<128, 6>::pvx(4) == -1, "P V steps in X");
 
 template <int D, bool CAUSAL, bool QK8>
 __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs args) {
   using Tl = SwzTile<D>;
   using Tl8 = SwzTile8<D>;
-  using S = Sched1<D>;
+  // E4M3: the S products take a quarter of phase X's steps, so part of P V moves there
+  using S = Sched1<D, (QK8 && D == 128) ? 6 : 0>;
+  constexpr int NPX = (QK8 && D == 128) ? 6 : 0;
   // padding before the max reads of the next tile's scores: in phase X they come three steps
   // (three products and their vector work) after the last product of key half 0, enough on
   // their own; in phase Y two products after the last one of key half 1, which needs 8 more
@@ -528,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       // the products read the scales a few instructions after the VALU shift wrote them
       asm volatile("s_nop 4" : "+v"(ksc[0]), "+v"(ksc[1]));
     }
-    bf16x8 vf[NY];
+    bf16x8 vf[4 * nD];
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NX>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -544,9 +565,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
       }
       if constexpr ((i & 1) && (i >> 1) >= LK && (i >> 1) < LK + Tl::loadsPerWave)
         ld.issue(vslot_p(jp, j, 1), Vr, (j + 1) * kBlockN, T, (i >> 1) - LK);
+      if constexpr (i + 2 < NX && S::pvx(i + 2) >= 0) vf[S::pvx(i + 2)] = v_frag(Vs, S::pvx(i + 2));
       if constexpr (i == NX - 2) {
-        vf[0] = v_frag(Vs, 0);
-        vf[1] = v_frag(Vs, 1);
+        vf[NPX] = v_frag(Vs, NPX);
+        vf[NPX + 1] = v_frag(Vs, NPX + 1);
       }
       if constexpr (!QK8) {
         if constexpr (kk == 0) mfma_s_first(sblk(nxt, kb), kf[i], qf[kk]);
@@ -556,6 +578,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
         constexpr int m = i / 4, kb8 = m / nK8, kk8 = m % nK8;
         if constexpr (m + 2 < nKF8) kf8[m + 2] = k_frag8(Kn, m + 2);
         mfma8_s<kk8 == 0, 2 * kk8>(sblk(nxt, kb8), kf8[m], qf8[kk8], ksc[kb8], qsc);
+      }
+      if constexpr (S::pvx(i) >= 0) {
+        constexpr int g = S::pvx(i);
+        mfma_o(acc[g % nD], vf[g], p[g / nD]);
       }
       // the step's VALU work follows its product, so consecutive products are evenly spaced
       __builtin_amdgcn_sched_barrier(0);
@@ -581,9 +607,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     bool any = false;
     static_for<0, NY>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      constexpr int cc = i / nD, db = i % nD;
-      if constexpr (i + 2 < NY) vf[i + 2] = v_frag(Vs, i + 2);
-      mfma_o(acc[db], vf[i], p[cc]);
+      constexpr int g = NPX + i, cc = g / nD, db = g % nD;
+      if constexpr (i + 2 < NY) vf[g + 2] = v_frag(Vs, g + 2);
+      mfma_o(acc[db], vf[g], p[cc]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (i == S::YM0) fence_n<FY>(sblk(nxt, 1));
       if constexpr (S::max_count(true, i) > 0)
@@ -624,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
     // the products below read P right after the VALU wrote it
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(p[2]), "+v"(p[3]));
 #pragma unroll
-    for (int g = 0; g < NY; ++g) mfma_o(acc[g % nD], v_frag(Vs, g), p[g / nD]);
+    for (int g = 0; g < 4 * nD; ++g) mfma_o(acc[g % nD], v_frag(Vs, g), p[g / nD]);
     // the products are inline asm, whose latency the compiler does not see: the padding sits
     // here, right after them, so that no register copy the compiler places where the callers'
     // paths join can read an accumulator before its product has written it
