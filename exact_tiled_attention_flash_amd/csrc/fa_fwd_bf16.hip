@@ -166,6 +166,49 @@ static_assert(Sched1<128>::valid() && Sched1<64>::valid() && Sched1<128, 6>::val
 static_assert(Sched1<128, 6>::pvx(2) == 0 && Sched1<128, 6>::pvx(11) == 5 &&
               Sched1<128, 6>::pvx(14) == -1 && Sched1<128, 6>::pvx(4) == -1, "P V steps in X");
 
+// Grid order of a packed batch of at most 64 sequences whose head-group count is a multiple
+// of 8. As in xcd_grid_item, unit r = b HG + hg stays on XCD r % 8 (workgroup L runs on XCD
+// L % 8), so every XCD holds HG / 8 units of every sequence. Within an XCD the sequences go in
+// order of decreasing work (query tiles times keys; ties by index), a sequence's tiles heaviest
+// first with its units fastest, so the longest causal tiles start first and the short
+// sequences fill the end of the launch. The items of an XCD are numbered without gaps, so the
+// grid needs only HG * (sum of the tile counts) workgroups instead of B * HG * (tiles of the
+// longest sequence). Every wave computes the same item from the offsets: lane b holds
+// sequence b, and each lane adds up the items of the sequences ordered before its own. False
+// when the index lies past the XCD's last item (the grid is sized on the host from total_q,
+// which bounds the tile count when the offsets do not decrease).
+__device__ __forceinline__ bool varlen_item(const FwdKArgs& a, int L, int qrows, int& r,
+                                            int& qt) {
+  const int b = lane_thread_id() & 63;
+  int nt = 0, tk = 0;
+  if (b < a.B) {
+    const int q0 = min(max(a.cu_q[b], 0), a.Tq);
+    const int q1 = min(max(a.cu_q[b + 1], q0), a.Tq);
+    const int k0 = min(max(a.cu_k[b], 0), a.Tk);
+    const int k1 = min(max(a.cu_k[b + 1], k0), a.Tk);
+    nt = min((q1 - q0 + qrows - 1) / qrows, a.nq);
+    tk = k1 - k0;
+  }
+  // units of a sequence on XCD x: head groups x, x + 8, ... (HG is a multiple of 8)
+  const int cnt = a.HG >> 3, items = cnt * nt;
+  const float key = (float)nt * (float)(tk + 1);   // work estimate, exact order not needed
+  int before = 0;
+  for (int b2 = 0; b2 < a.B; ++b2) {
+    const float k2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, key), b2));
+    const int i2 = __builtin_amdgcn_readlane(items, b2);
+    if (k2 > key || (k2 == key && b2 < b)) before += i2;
+  }
+  const int m = L >> 3;
+  const uint64_t own = __builtin_amdgcn_ballot_w64(items > 0 && before <= m && m < before + items);
+  if (own == 0) return false;
+  const int bs = (int)__builtin_ctzll(own);
+  const int w = m - __builtin_amdgcn_readlane(before, bs);
+  const int lvl = w / cnt;
+  qt = __builtin_amdgcn_readlane(nt, bs) - 1 - lvl;
+  r = bs * a.HG + (L & 7) + 8 * (w - lvl * cnt);
+  return true;
+}
+
 template <int D, bool CAUSAL, bool QK8>
 __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs args) {
   using Tl = SwzTile<D>;
@@ -203,15 +246,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   // head, 128 / hpw consecutive queries each; heaviest causal tile first. Within an XCD's
   // group of r the tiles walk the same keys at about the same time and share each K/V line.
   const int L = workgroup_id();
+  const int qrows = kBlockM >> args.hpw_log2;
   int r, qt;
-  xcd_grid_item(L, args.nbhg, args.nq, args.grp, r, qt);
-  if (CAUSAL) qt = args.nq - 1 - qt;
+  if (args.vsched) {
+    if (!varlen_item(args, L, qrows, r, qt)) return;   // uniform per workgroup
+  } else {
+    xcd_grid_item(L, args.nbhg, args.nq, args.grp, r, qt);
+    if (CAUSAL) qt = args.nq - 1 - qt;
+  }
   const int b = r / args.HG, hg = r % args.HG;
   const int hpw = 1 << args.hpw_log2;
   const int h0 = hg * hpw;
   const int hq = h0 + (wave & (hpw - 1));   // this wave's query head
   const int kvh = h0 / args.G;
-  const int qrows = kBlockM >> args.hpw_log2;
   int qs = 0, Tq = args.Tq, ks = 0, Tk = args.Tk;
   if (args.cu_q) {
     qs = min(max(args.cu_q[b], 0), args.Tq);
@@ -801,7 +848,17 @@ hipError_t launch(const FwdBf16Problem& p) {
     k.lse_bs = (int64_t)p.Hq * p.Tq;
   }
   k.c = p.scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL((fwd_q32_kernel<D, CAUSAL, QK8>), dim3(k.nq * k.nbhg), dim3(kThreads), 0, p.stream, k);
+  k.B = p.B;
+  int64_t grid = (int64_t)k.nq * k.nbhg;
+  // packed batches of up to 64 sequences (one per lane) with whole XCD shares of head groups:
+  // longest sequence first, no workgroups for tiles past a sequence's end (varlen_item)
+  if (p.cu_q && p.B <= 64 && k.HG % 8 == 0) {
+    const int64_t qr = kBlockM >> k.hpw_log2;
+    const int64_t tiles = ((int64_t)p.Tq + (int64_t)p.B * (qr - 1)) / qr;   // >= sum of tile counts
+    k.vsched = 1;
+    grid = (int64_t)k.HG * (tiles < (int64_t)p.B * k.nq ? tiles : (int64_t)p.B * k.nq);
+  }
+  hipLaunchKernelGGL((fwd_q32_kernel<D, CAUSAL, QK8>), dim3((unsigned)grid), dim3(kThreads), 0, p.stream, k);
   return hipGetLastError();
 }
 

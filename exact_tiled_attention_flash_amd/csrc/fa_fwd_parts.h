@@ -74,6 +74,8 @@ struct FwdKArgs {
   int nbhg;          // B * HG
   int nq;            // query tiles per (batch, head group)
   int grp;           // (batch, head group)s an XCD works through together (xcd_grid_item)
+  int B;             // sequences (packed) or batch size
+  int vsched;        // packed batch walked longest sequence first (varlen_item), else 0
   float c;           // scale * log2(e)
   // E4M3 Q K^T: codes of q / k (same layout and strides as q / k, one byte an element) and
   // their block scales (one byte per 32 elements of a row: element offset / 32)

@@ -138,19 +138,68 @@ def test_varlen_heads_in_groups_of_four_per_xcd(fa):
                f"varlen grouped causal={causal}")
 
 
-def test_varlen_equals_dense_when_lengths_match(fa):
-    # a packed batch of equal lengths is the dense call on the same data, bit for bit
-    B, H, T, D = 3, 4, 150, 128
-    d = synth.make_inputs(B, H, T, D, "bf16", seed=8)
-    q, k, v = (device_tensor(d[n], "bf16") for n in "qkv")
-    pack = lambda t: t.permute(0, 2, 1, 3).reshape(B * T, H, D).contiguous()
-    cu = torch.arange(0, (B + 1) * T, T, dtype=torch.int32, device="cuda")
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8)])
+def test_varlen_longest_first_order(fa, Hq, Hkv, causal, D):
+    """Head groups a multiple of 8 and at most 64 sequences: the grid that walks each XCD's
+    sequences longest first, with no workgroups past a sequence's end. Empty, one-row and
+    ragged sequences, query and key lengths that differ, equal lengths (ties in the order)."""
+    print(f"case varlen longest-first Hq={Hq} Hkv={Hkv} D={D} causal={causal}", flush=True)
+    lq = [40, 0, 300, 1, 129, 40, 77, 256, 5, 40]
+    lk = [40, 3, 300, 1, 500, 40, 20, 256, 0, 40]
+    qb, cq = _pack(lq, Hq, D, 31)
+    kb, ck = _pack(lk, Hkv, D, 32)
+    vb, _ = _pack(lk, Hkv, D, 33)
+    scale = 1 / math.sqrt(D)
+    o, lse = fa.fa_fwd_varlen(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                              device_tensor(vb, "bf16"), torch.from_numpy(cq).cuda(),
+                              torch.from_numpy(ck).cuda(), max(lq), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward_varlen(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                   as_f64(vb, "bf16"), cq, ck, scale, causal)
+    _check(host_f64(o), lse.cpu().numpy().astype(np.float64).T, o_ref, l_ref.T,
+           f"longest-first Hq={Hq} causal={causal}")
+
+
+@pytest.mark.parametrize("n_seq", [64, 65])
+def test_varlen_many_sequences(fa, n_seq):
+    """64 sequences (one a lane of the longest-first order) and 65 (the grouped grid order)."""
+    print(f"case varlen {n_seq} sequences", flush=True)
+    rng = np.random.default_rng(n_seq)
+    lens = [int(x) for x in rng.integers(0, 200, n_seq)]
+    lens[3] = 0
+    lens[10] = 1
+    H, D = 8, 64
+    qb, cu = _pack(lens, H, D, 41)
+    kb, _ = _pack(lens, H, D, 42)
+    vb, _ = _pack(lens, H, D, 43)
+    cu_d = torch.from_numpy(cu).cuda()
     for causal in (False, True):
-        o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
-        o2, l2 = fa.fa_fwd_varlen(pack(q), pack(k), pack(v), cu, cu, T, causal=causal)
+        o, lse = fa.fa_fwd_varlen(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                                  device_tensor(vb, "bf16"), cu_d, cu_d, max(lens), causal=causal,
+                                  scale=0.125)
         torch.cuda.synchronize()
-        assert torch.equal(pack(o1), o2)
-        assert torch.equal(l1.permute(1, 0, 2).reshape(H, B * T), l2)
+        o_ref, l_ref = oracle.attention_forward_varlen(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                       as_f64(vb, "bf16"), cu, cu, 0.125, causal)
+        _check(host_f64(o), lse.cpu().numpy().astype(np.float64).T, o_ref, l_ref.T,
+               f"{n_seq} sequences causal={causal}")
+
+
+def test_varlen_equals_dense_when_lengths_match(fa):
+    # a packed batch of equal lengths is the dense call on the same data, bit for bit (4 heads:
+    # the grouped grid order; 8 heads: longest first)
+    for B, H, T, D in ((3, 4, 150, 128), (3, 8, 150, 128)):
+        d = synth.make_inputs(B, H, T, D, "bf16", seed=8)
+        q, k, v = (device_tensor(d[n], "bf16") for n in "qkv")
+        pack = lambda t: t.permute(0, 2, 1, 3).reshape(B * T, H, D).contiguous()
+        cu = torch.arange(0, (B + 1) * T, T, dtype=torch.int32, device="cuda")
+        for causal in (False, True):
+            o1, l1 = fa.fa_fwd(q, k, v, causal=causal)
+            o2, l2 = fa.fa_fwd_varlen(pack(q), pack(k), pack(v), cu, cu, T, causal=causal)
+            torch.cuda.synchronize()
+            assert torch.equal(pack(o1), o2)
+            assert torch.equal(l1.permute(1, 0, 2).reshape(H, B * T), l2)
 
 
 def test_varlen_out_of_range_offsets_stay_in_bounds(fa):
