@@ -306,9 +306,13 @@ def config_rows(torch, fa, metrics, which, steps, warmup, seed, peak):
         flops = metrics.fwd_flops(w.B, w.H, w.T, w.D, w.causal)
         par.update({"tol_o": to, "tol_lse": tl, "compared": "whole tensors",
                     "pass": bool(par["max_abs_o"] <= to and par["max_abs_lse"] <= tl)})
+        # one workgroup per 128 query rows of a (b, h)
+        wgs = w.B * w.H * -(-w.T // 128)
         rows.setdefault(cfg, {})[name] = {
             "ms_per_step": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
-            "flops_per_step": flops, "bound": "launch latency (parity configuration)",
+            "flops_per_step": flops,
+            "bound": f"latency: {wgs} workgroups for 256 compute units, each walking every key "
+                     "tile of its rows in turn (parity configuration)",
             "parity": par,
             "oracle": {"seconds": round(el, 4), "tflops": round(flops / el / 1e12, 6),
                        "cores": _threads(), "sample": "whole workload"}}
