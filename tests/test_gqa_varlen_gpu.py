@@ -140,7 +140,7 @@ def test_varlen_heads_in_groups_of_four_per_xcd(fa):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8)])
 def test_varlen_longest_first_order(fa, Hq, Hkv, causal, D):
     """Head groups a multiple of 8 and at most 64 sequences: the grid that walks each XCD's
     sequences longest first, with no workgroups past a sequence's end. Empty, one-row and
