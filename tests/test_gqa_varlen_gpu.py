@@ -186,6 +186,34 @@ def test_varlen_many_sequences(fa, n_seq):
                f"{n_seq} sequences causal={causal}")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_varlen_random_batches(fa, seed):
+    """Random packed batches in the longest-first order: 1 to 64 sequences of 0 to 400 rows
+    (a fifth of them empty), query and key lengths drawn separately, random mask."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 65))
+    lq = rng.integers(0, 401, n)
+    lq[rng.random(n) < 0.2] = 0
+    lq[0] = max(int(lq[0]), 1)
+    lk = rng.integers(0, 401, n) if seed % 2 else lq.copy()
+    causal = bool(rng.integers(0, 2))
+    Hq, Hkv, D = 16, 8, 128
+    print(f"case varlen random seed={seed} n={n} causal={causal}", flush=True)
+    qb, cq = _pack(lq, Hq, D, 200 + seed)
+    kb, ck = _pack(lk, Hkv, D, 300 + seed)
+    vb, _ = _pack(lk, Hkv, D, 400 + seed)
+    scale = 1 / math.sqrt(D)
+    o, lse = fa.fa_fwd_varlen(device_tensor(qb, "bf16"), device_tensor(kb, "bf16"),
+                              device_tensor(vb, "bf16"), torch.from_numpy(cq).cuda(),
+                              torch.from_numpy(ck).cuda(), int(lq.max()), causal=causal,
+                              scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_forward_varlen(as_f64(qb, "bf16"), as_f64(kb, "bf16"),
+                                                   as_f64(vb, "bf16"), cq, ck, scale, causal)
+    _check(host_f64(o), lse.cpu().numpy().astype(np.float64).T, o_ref, l_ref.T,
+           f"random batch seed={seed}")
+
+
 def test_varlen_equals_dense_when_lengths_match(fa):
     # a packed batch of equal lengths is the dense call on the same data, bit for bit (4 heads:
     # the grouped grid order; 8 heads: longest first)
