@@ -166,8 +166,8 @@ static_assert(Sched1<128>::valid() && Sched1<64>::valid() && Sched1<128, 6>::val
 static_assert(Sched1<128, 6>::pvx(2) == 0 && Sched1<128, 6>::pvx(11) == 5 &&
               Sched1<128, 6>::pvx(14) == -1 && Sched1<128, 6>::pvx(4) == -1, "P V steps in X");
 
-// Grid order of a packed batch of at most 64 sequences whose head-group count is a multiple
-// of 8. As in xcd_grid_item, unit r = b HG + hg stays on XCD r % 8 (workgroup L runs on XCD
+// Grid order of a skewed packed batch of at most 64 sequences whose head-group count is a
+// multiple of 8 (the host picks it; see the launch). As in xcd_grid_item, unit r = b HG + hg stays on XCD r % 8 (workgroup L runs on XCD
 // L % 8), so every XCD holds HG / 8 units of every sequence. Within an XCD the sequences go in
 // order of decreasing work (query tiles times keys; ties by index), a sequence's tiles heaviest
 // first with its units fastest, so the longest causal tiles start first and the short
@@ -176,27 +176,31 @@ static_assert(Sched1<128, 6>::pvx(2) == 0 && Sched1<128, 6>::pvx(11) == 5 &&
 // longest sequence). Every wave computes the same item from the offsets: lane b holds
 // sequence b, and each lane adds up the items of the sequences ordered before its own. False
 // when the index lies past the XCD's last item (the grid is sized on the host from total_q,
-// which bounds the tile count when the offsets do not decrease).
-__device__ __forceinline__ bool varlen_item(const FwdKArgs& a, int L, int qrows, int& r,
-                                            int& qt) {
+// which bounds the tile count when the offsets do not decrease). Also returns the chosen
+// sequence's first query and key rows and its lengths (clamped as for the other grid order).
+__device__ __forceinline__ bool varlen_item(const FwdKArgs& a, int L, int qrows, int& r, int& qt,
+                                            int& qs, int& tq, int& ks, int& tk) {
   const int b = lane_thread_id() & 63;
-  int nt = 0, tk = 0;
+  int nt = 0, q0 = 0, lq = 0, k0 = 0, lk = 0;
   if (b < a.B) {
-    const int q0 = min(max(a.cu_q[b], 0), a.Tq);
-    const int q1 = min(max(a.cu_q[b + 1], q0), a.Tq);
-    const int k0 = min(max(a.cu_k[b], 0), a.Tk);
-    const int k1 = min(max(a.cu_k[b + 1], k0), a.Tk);
-    nt = min((q1 - q0 + qrows - 1) / qrows, a.nq);
-    tk = k1 - k0;
+    q0 = min(max(a.cu_q[b], 0), a.Tq);
+    lq = min(max(a.cu_q[b + 1], q0), a.Tq) - q0;
+    k0 = min(max(a.cu_k[b], 0), a.Tk);
+    lk = min(max(a.cu_k[b + 1], k0), a.Tk) - k0;
+    nt = min((lq + qrows - 1) / qrows, a.nq);
   }
   // units of a sequence on XCD x: head groups x, x + 8, ... (HG is a multiple of 8)
   const int cnt = a.HG >> 3, items = cnt * nt;
-  const float key = (float)nt * (float)(tk + 1);   // work estimate, exact order not needed
+  // order key: the work estimate (query tiles x keys; a non-negative float, so its bits order
+  // as integers) with its low 6 bits replaced by 63 - b, so that every key differs and near
+  // ties go by index; branch-free, a few instructions per sequence
+  const float work = (float)nt * (float)(lk + 1);
+  const uint32_t key = (__builtin_bit_cast(uint32_t, work) & ~63u) | (uint32_t)(63 - b);
   int before = 0;
   for (int b2 = 0; b2 < a.B; ++b2) {
-    const float k2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, key), b2));
+    const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key, b2);
     const int i2 = __builtin_amdgcn_readlane(items, b2);
-    if (k2 > key || (k2 == key && b2 < b)) before += i2;
+    before += k2 > key ? i2 : 0;
   }
   const int m = L >> 3;
   const uint64_t own = __builtin_amdgcn_ballot_w64(items > 0 && before <= m && m < before + items);
@@ -206,6 +210,10 @@ __device__ __forceinline__ bool varlen_item(const FwdKArgs& a, int L, int qrows,
   const int lvl = w / cnt;
   qt = __builtin_amdgcn_readlane(nt, bs) - 1 - lvl;
   r = bs * a.HG + (L & 7) + 8 * (w - lvl * cnt);
+  qs = __builtin_amdgcn_readlane(q0, bs);
+  tq = __builtin_amdgcn_readlane(lq, bs);
+  ks = __builtin_amdgcn_readlane(k0, bs);
+  tk = __builtin_amdgcn_readlane(lk, bs);
   return true;
 }
 
@@ -248,8 +256,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   const int L = workgroup_id();
   const int qrows = kBlockM >> args.hpw_log2;
   int r, qt;
+  int qs = 0, Tq = args.Tq, ks = 0, Tk = args.Tk;
   if (args.vsched) {
-    if (!varlen_item(args, L, qrows, r, qt)) return;   // uniform per workgroup
+    if (!varlen_item(args, L, qrows, r, qt, qs, Tq, ks, Tk)) return;   // uniform per workgroup
   } else {
     xcd_grid_item(L, args.nbhg, args.nq, args.grp, r, qt);
     if (CAUSAL) qt = args.nq - 1 - qt;
@@ -259,8 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_q32_kernel(const FwdKArgs arg
   const int h0 = hg * hpw;
   const int hq = h0 + (wave & (hpw - 1));   // this wave's query head
   const int kvh = h0 / args.G;
-  int qs = 0, Tq = args.Tq, ks = 0, Tk = args.Tk;
-  if (args.cu_q) {
+  if (args.cu_q && !args.vsched) {
     qs = min(max(args.cu_q[b], 0), args.Tq);
     Tq = min(max(args.cu_q[b + 1], qs), args.Tq) - qs;
     ks = min(max(args.cu_k[b], 0), args.Tk);
@@ -850,9 +858,12 @@ hipError_t launch(const FwdBf16Problem& p) {
   k.c = p.scale * 1.44269504088896340736f;
   k.B = p.B;
   int64_t grid = (int64_t)k.nq * k.nbhg;
-  // packed batches of up to 64 sequences (one per lane) with whole XCD shares of head groups:
-  // longest sequence first, no workgroups for tiles past a sequence's end (varlen_item)
-  if (p.cu_q && p.B <= 64 && k.HG % 8 == 0) {
+  // skewed packed batches (the longest sequence at least 2048 rows and at least 2.5 times the
+  // mean length) of up to 64 sequences (one per lane) with whole XCD shares of head groups:
+  // longest sequence first, no workgroups for tiles past a sequence's end (varlen_item). Batches
+  // of even or short lengths keep the grouped order, which measured faster for them.
+  if (p.cu_q && p.B <= 64 && k.HG % 8 == 0 && p.max_q >= 2048 &&
+      (int64_t)p.Tq * 5 <= (int64_t)p.B * p.max_q * 2) {
     const int64_t qr = kBlockM >> k.hpw_log2;
     const int64_t tiles = ((int64_t)p.Tq + (int64_t)p.B * (qr - 1)) / qr;   // >= sum of tile counts
     k.vsched = 1;

@@ -127,10 +127,11 @@ int fa_fwd_gqa(const void *q, const void *k, const void *v, void *o, float *lse,
  *   max_seqlen_q  bound on every query length (sizes the grid; rows of a
  *               longer sequence beyond it are left unwritten)
  * Heads and masking as fa_fwd_gqa, per sequence. Rows not covered by any
- * sequence are left unwritten. The offsets are expected not to decrease: with up
- * to 64 sequences and a multiple of 8 query-head groups (Hq, or Hq / 2 or
- * Hq / 4 when Hq / Hkv is a multiple of 2 or 4) the grid is sized from total_q,
- * and sequences that overlap may then leave some of their rows unwritten.
+ * sequence are left unwritten. The offsets are expected not to decrease: for a
+ * skewed batch (max_seqlen_q >= 2048 and at least 2.5 times total_q / B) of up to
+ * 64 sequences with a multiple of 8 query-head groups (Hq, or Hq / 2 or Hq / 4
+ * when Hq / Hkv is a multiple of 2 or 4) the grid is sized from total_q, and
+ * sequences that overlap may then leave some of their rows unwritten.
  * Source: "Triton FlashAttention-2 forward", "Exercises" (a cu_seqlens index
  * tensor packs requests of different lengths into one launch).
  */

@@ -138,16 +138,16 @@ def test_varlen_heads_in_groups_of_four_per_xcd(fa):
                f"varlen grouped causal={causal}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 8), (32, 8)])
-def test_varlen_longest_first_order(fa, Hq, Hkv, causal, D):
-    """Head groups a multiple of 8 and at most 64 sequences: the grid that walks each XCD's
-    sequences longest first, with no workgroups past a sequence's end. Empty, one-row and
-    ragged sequences, query and key lengths that differ, equal lengths (ties in the order)."""
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (8, 8, 128), (16, 8, 128), (32, 8, 64)])
+def test_varlen_longest_first_order(fa, Hq, Hkv, D, causal):
+    """Skewed batches (the longest sequence at least 2048 rows and 2.5 times the mean), at most 64
+    sequences, head groups a multiple of 8: the grid that walks each XCD's sequences longest
+    first, with no workgroups past a sequence's end. Empty, one-row and ragged sequences, query
+    and key lengths that differ, equal lengths (ties in the order)."""
     print(f"case varlen longest-first Hq={Hq} Hkv={Hkv} D={D} causal={causal}", flush=True)
-    lq = [40, 0, 300, 1, 129, 40, 77, 256, 5, 40]
-    lk = [40, 3, 300, 1, 500, 40, 20, 256, 0, 40]
+    lq = [40, 0, 2049, 1, 129, 40, 77, 256, 5, 40]
+    lk = [40, 3, 2049, 1, 500, 40, 20, 256, 0, 40]
     qb, cq = _pack(lq, Hq, D, 31)
     kb, ck = _pack(lk, Hkv, D, 32)
     vb, _ = _pack(lk, Hkv, D, 33)
@@ -164,12 +164,14 @@ def test_varlen_longest_first_order(fa, Hq, Hkv, causal, D):
 
 @pytest.mark.parametrize("n_seq", [64, 65])
 def test_varlen_many_sequences(fa, n_seq):
-    """64 sequences (one a lane of the longest-first order) and 65 (the grouped grid order)."""
+    """64 sequences (one a lane of the longest-first order) and 65 (the grouped grid order), one
+    of them 2100 rows long."""
     print(f"case varlen {n_seq} sequences", flush=True)
     rng = np.random.default_rng(n_seq)
     lens = [int(x) for x in rng.integers(0, 200, n_seq)]
     lens[3] = 0
     lens[10] = 1
+    lens[20] = 2100
     H, D = 8, 64
     qb, cu = _pack(lens, H, D, 41)
     kb, _ = _pack(lens, H, D, 42)
@@ -188,17 +190,20 @@ def test_varlen_many_sequences(fa, n_seq):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_varlen_random_batches(fa, seed):
-    """Random packed batches in the longest-first order: 1 to 64 sequences of 0 to 400 rows
-    (a fifth of them empty), query and key lengths drawn separately, random mask."""
+    """Random packed batches of 1 to 64 sequences of 0 to 400 rows (a fifth of them empty), query
+    and key lengths drawn separately, random mask; even seeds add one sequence of 2048-2300 rows
+    (a skewed batch: the longest-first order), odd ones keep the grouped order."""
     rng = np.random.default_rng(100 + seed)
     n = int(rng.integers(1, 65))
     lq = rng.integers(0, 401, n)
     lq[rng.random(n) < 0.2] = 0
     lq[0] = max(int(lq[0]), 1)
-    lk = rng.integers(0, 401, n) if seed % 2 else lq.copy()
+    if seed % 2 == 0:
+        lq[int(rng.integers(0, n))] = int(rng.integers(2048, 2301))
+    lk = rng.integers(0, 401, n) if seed % 3 else lq.copy()
     causal = bool(rng.integers(0, 2))
     Hq, Hkv, D = 16, 8, 128
-    print(f"case varlen random seed={seed} n={n} causal={causal}", flush=True)
+    print(f"case varlen random seed={seed} n={n} max={int(lq.max())} causal={causal}", flush=True)
     qb, cq = _pack(lq, Hq, D, 200 + seed)
     kb, ck = _pack(lk, Hkv, D, 300 + seed)
     vb, _ = _pack(lk, Hkv, D, 400 + seed)
