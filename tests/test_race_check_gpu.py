@@ -127,6 +127,20 @@ def test_grouped_packed_fp8_decode_bitwise_equal(libs, causal):
         outs.append((o, lse))
     _same(*outs, "packed")
 
+    # a skewed batch with 8 head groups: the longest-first grid order
+    lens = [2100, 1, 0, 129, 300]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    tot = int(sum(lens))
+    qp, kp, vp = bf((tot, 8, D)), bf((tot, 8, D)), bf((tot, 8, D))
+    outs = []
+    for lib in (rel, chk):
+        o, lse = torch.zeros_like(qp), torch.zeros((8, tot), device="cuda")
+        assert lib.fa_fwd_varlen(qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), cu.data_ptr(), cu.data_ptr(), len(lens), 8, 8,
+                                 tot, tot, max(lens), D, _f(0.09), int(causal), 1, _stream()) == 0
+        outs.append((o, lse))
+    _same(*outs, "packed, skewed")
+
     q8 = torch.empty((B, Hq, Tq, D), dtype=torch.uint8, device="cuda")
     qs = torch.empty((B, Hq, Tq, D // 32), dtype=torch.uint8, device="cuda")
     k8 = torch.empty((B, Hkv, Tk, D), dtype=torch.uint8, device="cuda")
