@@ -25,6 +25,9 @@
 //   * The partials go to the workspace as fp32: acc [split][M][D] and (m, l, l_rounded) per
 //     row, with m in the exp2 domain (scores times scale * log2 e). The merge kernel gives
 //     each output row one workgroup of 256 threads, which read several splits at once.
+//   * With per-sequence lengths (up to 64 sequences) the split slots of a K/V head are shared
+//     out in proportion to the sequences' lengths (dec_plan), so that every split streams about
+//     the same number of key tiles.
 //   * As in the forward kernel, P is rounded to bf16 before the P V product; O is normalised
 //     by the sum of the rounded P and LSE uses the fp32 sum of the unrounded exponentials.
 
@@ -47,7 +50,48 @@ struct DecKArgs {
   int nsplit, nwork;          // splits per (b, K/V head); nwork = B * Hkv * nsplit
   float c;                    // scale * log2(e)
   int causal;
+  int B;
+  int bal;                    // split slots shared out by length (dec_plan), else 0
 };
+
+constexpr int kMaxSplit = 1024;   // splits of one (b, K/V head) the merge can take
+
+// Sum of x over the 64 lanes of the wave, as a wave-uniform value: DPP exchanges within each
+// row of 16 lanes (pairs, quads, half-row mirror, row mirror), then the four row sums. Needs
+// every lane active.
+__device__ __forceinline__ int wave_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xb1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4e, 0xf, 0xf, false);    // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);   // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false);   // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+// Split plan of a batch with per-sequence lengths (at most 64 sequences, lane b holds sequence
+// b). With one split count for every sequence, the splits of a short sequence are short and
+// the long sequences' splits run on alone at the end. Here the B * nsplit split slots of each
+// K/V head are shared out in proportion to the sequences' key tiles: sequence b gets
+// ns = 1 + (B * nsplit - B) * nt_b / (sum of nt) slots (at most kMaxSplit), the slots
+// first .. first + ns - 1 in sequence order, so every split walks about the same number of
+// tiles and the slots left over run nothing. Both kernels compute the same plan from the
+// lengths. Needs every lane active.
+struct DecPlan {
+  int nt, ns, first;   // this lane's sequence: key tiles, splits, first slot
+};
+__device__ __forceinline__ DecPlan dec_plan(const int* seqlens, int B, int Tk, int nsplit) {
+  const int b = lane_thread_id() & 63;
+  DecPlan p{0, 0, 0};
+  if (b < B) p.nt = (min(max(seqlens[b], 0), Tk) + kKeys - 1) / kKeys;
+  const int tot = wave_sum(p.nt);
+  if (b < B)
+    p.ns = min(1 + (tot > 0 ? (int)((int64_t)(B * nsplit - B) * p.nt / tot) : 0), kMaxSplit);
+  for (int b2 = 0; b2 < B; ++b2) {
+    const int n2 = __builtin_amdgcn_readlane(p.ns, b2);
+    p.first += b2 < b ? n2 : 0;
+  }
+  return p;
+}
 
 // Direct HBM -> LDS loads of one 32-row tile of a (rows x D) matrix by a single wave, into the
 // swizzled layout of SwzTile (rows 0..31). Lane `lane` of load i fills tile bytes [16 u,
@@ -146,14 +190,31 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(const DecKArgs a) {
   const int l32 = lane & 31, h = lane >> 5;
   const int gw = workgroup_id();
   if (gw >= a.nwork) return;
-  const int split = gw % a.nsplit;
-  const int bh = gw / a.nsplit;   // b * Hkv + K/V head
-  const int b = bh / a.Hkv, kvh = bh % a.Hkv;
-  int L = a.Tk;
-  if (a.seqlens) L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.Tk));
+  int b, kvh, split, nsp, L = a.Tk;
+  if (a.bal) {
+    // slot j of K/V head kvh belongs to the sequence whose range of slots holds it
+    const int per = a.nwork / a.Hkv;   // B * nsplit slots a K/V head
+    kvh = gw / per;
+    const int j = gw - kvh * per;
+    const DecPlan pl = dec_plan(a.seqlens, a.B, a.Tk, a.nsplit);
+    const uint64_t own = __builtin_amdgcn_ballot_w64(pl.ns > 0 && pl.first <= j && j < pl.first + pl.ns);
+    if (own == 0) return;   // a slot left over: no partial, the merge does not read it
+    b = (int)__builtin_ctzll(own);
+    split = j - __builtin_amdgcn_readlane(pl.first, b);
+    nsp = __builtin_amdgcn_readlane(pl.ns, b);
+    L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.Tk));
+  } else {
+    split = gw % a.nsplit;
+    const int bh0 = gw / a.nsplit;   // b * Hkv + K/V head
+    b = bh0 / a.Hkv;
+    kvh = bh0 % a.Hkv;
+    nsp = a.nsplit;
+    if (a.seqlens) L = __builtin_amdgcn_readfirstlane(min(max(a.seqlens[b], 0), a.Tk));
+  }
+  const int bh = b * a.Hkv + kvh;
   const int nt = (L + kKeys - 1) / kKeys;
-  const int t0 = (int)((int64_t)split * nt / a.nsplit);
-  const int t1 = (int)((int64_t)(split + 1) * nt / a.nsplit);
+  const int t0 = (int)((int64_t)split * nt / nsp);
+  const int t1 = (int)((int64_t)(split + 1) * nt / nsp);
 
   const int64_t kv_off = (int64_t)bh * a.Tk * D;
   const uint16_t* Kh = a.k + kv_off;
@@ -338,10 +399,11 @@ struct MergeKArgs {
   uint16_t* o;
   float* lse;
   int Hq, Hkv, G, Tq, M, nsplit, nwork, rows;   // rows = B * Hq * Tq
+  const int* seqlens;                           // with bal: the split plan's lengths
+  int B, Tk, bal;
 };
 
 constexpr int kMergeThreads = 256;
-constexpr int kMaxSplit = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const MergeKArgs a) {
@@ -358,12 +420,18 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Merge
   const int b = R / (a.Tq * a.Hq);
   const int kvh = hq / a.G, g = hq % a.G;
   const int r = g * a.Tq + qi;                                   // row within the K/V group
-  const int64_t w0 = ((int64_t)b * a.Hkv + kvh) * a.nsplit;     // first split's work index
+  int64_t w0 = ((int64_t)b * a.Hkv + kvh) * a.nsplit;           // first split's work index
+  int nsp = a.nsplit;
+  if (a.bal) {   // this sequence's slots of the split plan
+    const DecPlan pl = dec_plan(a.seqlens, a.B, a.Tk, a.nsplit);
+    w0 = (int64_t)kvh * (a.nwork / a.Hkv) + __builtin_amdgcn_readlane(pl.first, b);
+    nsp = __builtin_amdgcn_readlane(pl.ns, b);
+  }
   const float* St = a.part + (int64_t)a.nwork * a.M * D;
 
   // global max of the splits' m (exp2 domain)
   float mx = kNegInf;
-  for (int s = tid; s < a.nsplit; s += kMergeThreads) mx = fmaxf(mx, St[((w0 + s) * a.M + r) * 4]);
+  for (int s = tid; s < nsp; s += kMergeThreads) mx = fmaxf(mx, St[((w0 + s) * a.M + r) * 4]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if (lane == 0) red[0][wave] = mx;
@@ -372,7 +440,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Merge
   // weights; a split that saw no key (m = -inf) weighs 0, and so does every split of a row
   // that saw none (then O = 0, LSE = -inf)
   float sl = 0.f, slr = 0.f;
-  for (int s = tid; s < a.nsplit; s += kMergeThreads) {
+  for (int s = tid; s < nsp; s += kMergeThreads) {
     const f32x4 st = *reinterpret_cast<const f32x4*>(St + ((w0 + s) * a.M + r) * 4);
     const float w = st[0] == kNegInf ? 0.f : exp2_fast(st[0] - mx);
     wsh[s] = w;
@@ -394,14 +462,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Merge
   const int64_t stride = (int64_t)a.M * D;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   int s = sg;
-  for (; s + 3 * NG < a.nsplit; s += 4 * NG) {
+  for (; s + 3 * NG < nsp; s += 4 * NG) {
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(A + s * stride);
     const f32x4 x1 = *reinterpret_cast<const f32x4*>(A + (s + NG) * stride);
     const f32x4 x2 = *reinterpret_cast<const f32x4*>(A + (s + 2 * NG) * stride);
     const f32x4 x3 = *reinterpret_cast<const f32x4*>(A + (s + 3 * NG) * stride);
     acc += wsh[s] * x0 + wsh[s + NG] * x1 + wsh[s + 2 * NG] * x2 + wsh[s + 3 * NG] * x3;
   }
-  for (; s < a.nsplit; s += NG) acc += wsh[s] * *reinterpret_cast<const f32x4*>(A + s * stride);
+  for (; s < nsp; s += NG) acc += wsh[s] * *reinterpret_cast<const f32x4*>(A + s * stride);
   part_o[sg][c4] = acc;
   __syncthreads();
   if (tid < C4) {
@@ -429,13 +497,16 @@ hipError_t launch_decode_d(const DecodeBf16Problem& p) {
   DecKArgs ka{static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
               static_cast<const uint16_t*>(p.v), static_cast<float*>(p.workspace), p.seqlens,
               p.Hq, p.Hkv, G, p.Tq, p.Tk, M, p.nsplit, nwork, p.scale * 1.4426950408889634f,
-              p.causal ? 1 : 0};
+              p.causal ? 1 : 0, p.B, 0};
+  // per-sequence lengths, at most 64 sequences: split slots shared out by length (dec_plan)
+  const int bal = p.seqlens && p.B <= 64 ? 1 : 0;
+  ka.bal = bal;
   hipLaunchKernelGGL((decode_bf16_kernel<D, kSlots>), dim3(nwork), dim3(64), 0, p.stream, ka);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rows = p.B * p.Hq * p.Tq;
   MergeKArgs ma{static_cast<const float*>(p.workspace), static_cast<uint16_t*>(p.o), p.lse, p.Hq,
-                p.Hkv, G, p.Tq, M, p.nsplit, nwork, rows};
+                p.Hkv, G, p.Tq, M, p.nsplit, nwork, rows, p.seqlens, p.B, p.Tk, bal};
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(rows), dim3(kMergeThreads), 0, p.stream, ma);
   return hipGetLastError();
 }
