@@ -84,6 +84,19 @@ def test_decode_cache_lengths(fa, causal):
     assert np.all(o[0] == 0) and np.all(lse[0] == -np.inf)
 
 
+@pytest.mark.parametrize("n_seq,splits", [(64, 0), (64, 1), (64, 3), (65, 0), (7, 1000)])
+def test_decode_many_lengths(fa, n_seq, splits):
+    # up to 64 sequences: split slots shared out by length; 65: one split count for all. Lengths
+    # from empty to the whole cache, with automatic, single, few and very many split slots
+    print(f"case decode {n_seq} lengths splits={splits}", flush=True)
+    rng = np.random.default_rng(n_seq + splits)
+    lens = [int(x) for x in rng.integers(0, 700, n_seq)]
+    lens[0], lens[1], lens[-1] = 0, 700, 1
+    o, lse, o_ref, l_ref = _run(fa, n_seq, 8, 2, 1, 700, 64, True, lens=lens, splits=splits,
+                                seed=13)
+    _check(o, lse, o_ref, l_ref, f"{n_seq} lengths splits={splits}")
+
+
 def test_decode_negative_length_is_empty(fa):
     o, lse, o_ref, l_ref = _run(fa, 2, 4, 4, 1, 64, 64, False, lens=[-5, 64], seed=6)
     _check(o, lse, o_ref, l_ref, "negative length")
