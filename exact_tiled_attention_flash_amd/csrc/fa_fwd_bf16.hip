@@ -167,8 +167,9 @@ static_assert(Sched1<128, 6>::pvx(2) == 0 && Sched1<128, 6>::pvx(11) == 5 &&
               Sched1<128, 6>::pvx(14) == -1 && Sched1<128, 6>::pvx(4) == -1, "P V steps in X");
 
 // Grid order of a skewed packed batch of at most 64 sequences whose head-group count is a
-// multiple of 8 (the host picks it; see the launch). As in xcd_grid_item, unit r = b HG + hg stays on XCD r % 8 (workgroup L runs on XCD
-// L % 8), so every XCD holds HG / 8 units of every sequence. Within an XCD the sequences go in
+// multiple of 8 (the host picks it; see the launch). As in xcd_grid_item, unit r = b HG + hg
+// stays on XCD r % 8 (workgroup L runs on XCD L % 8), so every XCD holds HG / 8 units of every
+// sequence. Within an XCD the sequences go in
 // order of decreasing work (query tiles times keys; ties by index), a sequence's tiles heaviest
 // first with its units fastest, so the longest causal tiles start first and the short
 // sequences fill the end of the launch. The items of an XCD are numbered without gaps, so the
