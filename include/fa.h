@@ -204,7 +204,10 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D,
  *   num_splits  key splits per (b, K/V head); 0 = automatic: the smallest
  *               count that gives about 512 (b, K/V head, split) workgroups
  *               when cache_seqlens is NULL and about 1024 when it is given,
- *               within the bounds above
+ *               within the bounds above. With cache_seqlens and B <= 64 the
+ *               B * splits workgroups of each K/V head are shared out among
+ *               the sequences in proportion to their valid keys (at least one
+ *               each), so a long sequence gets more of them than a short one
  * Causal masking is aligned at the bottom right of each sequence's valid keys
  * L: query i sees key j iff j <= i + (L - Tq). A query that sees no key gets
  * o = 0 and lse = -inf. Two kernels: the splits write their partial (max, sum,
